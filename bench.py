@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Benchmark of MQA int8-KV decode on one MI355X.
+
+One step = one decode step of two attention layers that share ONE int8 KV
+buffer (cross-layer KV sharing): the new token's K and V rows are quantized
+into the buffer (kv_quantize_int8 x2), then a global layer and a
+sliding-window (1024) layer each run mqa_decode over it. Shapes: B = 64
+sequences of 4096 keys, 32 query heads, one KV head, head_dim 128.
+
+Inputs are synthetic (seeded N(0,1) on the device, K/V encoded with the
+library's own quantizer) and resident in HBM before timing. The step is
+rotated over enough buffer copies (>= 1 GB) that the 256 MB Infinity Cache
+cannot serve the KV reads. Steps are captured in a HIP graph so the timing is
+the GPU's, not Python's.
+
+Prints ONE JSON line. ``value`` = decode tokens/s of the step (B tokens per
+step, attention only). ``roofline`` describes the global-layer mqa_decode
+call (partition kernel + merge kernel). ``cpu_baseline`` times the CPU oracle
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, datasheet
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, datasheet
+METRIC = "MQA int8-KV decode: KV-read HBM GB/s (% of peak) and decode tokens/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--no-extra", action="store_true", help="skip the hybrid/long/prefill lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
+    ap.add_argument("--only", choices=["decode", "hybrid", "long", "prefill"], default=None,
+                    help="time a single workload (for profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on the stream the kernels run on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record(self.stream)
+
+    def stop_ms(self):
+        self.b.record(self.stream)
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def make_decode_buffers(torch, m, B, L, D, copies, gen):
+    """`copies` KV buffers filled with N(0,1) rows encoded by kv_quantize_int8."""
+    bufs = []
+    start = torch.zeros(B, dtype=torch.int32, device="cuda")
+    chunk = max(1, (1 << 28) // (L * D * 4))          # <= 256 MiB of fp32 at a time
+    for _ in range(copies):
+        kv = m.KVView.empty(B, L, D)
+        for b0 in range(0, B, chunk):
+            b1 = min(B, b0 + chunk)
+            for dst, dsc in ((kv.k, kv.k_scale), (kv.v, kv.v_scale)):
+                x = torch.randn((b1 - b0, L, D), generator=gen, device="cuda", dtype=torch.float32)
+                m.kv_quantize_int8(x, dst[b0:b1], dsc[b0:b1], start[b0:b1])
+        bufs.append(kv)
+    torch.cuda.synchronize()
+    return bufs
+
+
+def run_steps(torch, fn, steps, use_graph, stream):
+    """Replay `fn` (which runs `period` steps) steps/period times; returns ms."""
+    timer = Timer(torch, stream)
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        torch.cuda.synchronize()
+        reps = steps
+        g.replay()
+        torch.cuda.synchronize()
+        timer.start()
+        for _ in range(reps):
+            g.replay()
+        ms = timer.stop_ms()
+        return ms, g
+    timer.start()
+    for _ in range(steps):
+        fn()
+    return timer.stop_ms(), None
+
+
+def bench_decode(torch, m, acct, args, stream):
+    B, Hq, D, L = 64, 32, 128, 4096
+    windows = (0, 1024)
+    bytes_per_copy = B * L * (2 * D + 8)
+    R = max(2, math.ceil((1 << 30) / bytes_per_copy))              # >= 1 GiB of KV
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2)
+    bufs = make_decode_buffers(torch, m, B, L, D, R, gen)
+    seq_lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    start_pos = seq_lens - 1
+    q = [[torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in windows]
+         for _ in range(R)]
+    knew = [torch.randn((B, 1, D), generator=gen, device="cuda") for _ in range(R)]
+    vnew = [torch.randn((B, 1, D), generator=gen, device="cuda") for _ in range(R)]
+    outs = [torch.empty((B, Hq, D), device="cuda") for _ in windows]
+    ws = [m.decode_workspace(B, Hq, D, L, w) for w in windows]
+
+    def one_step(r):
+        kv = bufs[r]
+        m.kv_quantize_int8(knew[r], kv.k, kv.k_scale, start_pos)
+        m.kv_quantize_int8(vnew[r], kv.v, kv.v_scale, start_pos)
+        for li, w in enumerate(windows):
+            m.mqa_decode(q[r][li], kv, seq_lens, L, w, out=outs[li], workspace=ws[li])
+
+    def period():
+        for r in range(R):
+            one_step(r)
+
+    def global_only():
+        for r in range(R):
+            m.mqa_decode(q[r][0], bufs[r], seq_lens, L, 0, out=outs[0], workspace=ws[0])
+
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup // R)):
+            period()
+        torch.cuda.synchronize()
+        use_graph = not args.no_graph
+        reps = max(1, args.steps // R)
+        ms, _ = run_steps(torch, period, reps, use_graph, stream)
+        steps_done = reps * R
+        ms_step = ms / steps_done
+        # dominant kernel: the global layer's mqa_decode (partition + merge)
+        ms_g, _ = run_steps(torch, global_only, reps, use_graph, stream)
+        ms_call = ms_g / (reps * R)
+    kv_step = sum(acct.decode_kv_bytes([L] * B, w, D) for w in windows)
+    kv_global = acct.decode_kv_bytes([L] * B, 0, D)
+    res = {
+        "steps_done": steps_done, "ms_per_step": ms_step, "tokens_per_s": B / (ms_step * 1e-3),
+        "kv_bytes_per_step": kv_step, "step_kv_GBps": kv_step / (ms_step * 1e-3) / 1e9,
+        "global_call_us": ms_call * 1e3, "global_kv_bytes": kv_global,
+        "global_GBps": kv_global / (ms_call * 1e-3) / 1e9, "rotation_copies": R,
+        "graph": use_graph,
+    }
+    return res
+
+
+def bench_hybrid(torch, m, acct, stream):
+    """6-layer block: 1 global + 5 window-1024 layers, buffers G (l0), A (l1-3), B (l4-5)."""
+    import numpy as np
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import synth
+    w = synth.HYBRID
+    B, Hq, D = w.B, w.Hq, w.D
+    lens = w.lens()
+    L = int(lens.max())
+    L_cap = (L + 15) // 16 * 16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    bufs = {name: make_decode_buffers(torch, m, B, L_cap, D, 1, gen)[0] for name in ("G", "A", "Bf")}
+    seq_lens = torch.from_numpy(lens).cuda()
+    start_pos = seq_lens - 1
+    q = [torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in w.layers]
+    knew = torch.randn((B, 1, D), generator=gen, device="cuda")
+    vnew = torch.randn((B, 1, D), generator=gen, device="cuda")
+    out = torch.empty((B, Hq, D), device="cuda")
+    ws = torch.zeros(max(m.mqa_decode_workspace_bytes(B, Hq, D, L, win) for _, win in w.layers) + 16,
+                     dtype=torch.uint8, device="cuda")
+    owners = {}
+    for li, (name, _) in enumerate(w.layers):
+        owners.setdefault(name, li)
+
+    def block():
+        for li, (name, win) in enumerate(w.layers):
+            kv = bufs[name]
+            if owners[name] == li:             # first layer of a sharing group writes the token
+                m.append_kv(kv, knew, vnew, start_pos)
+            m.mqa_decode(q[li], kv, seq_lens, L, win, out=out, workspace=ws)
+
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            block()
+        torch.cuda.synchronize()
+        reps = 30
+        ms, _ = run_steps(torch, block, reps, True, stream)
+    ms_block = ms / reps
+    kv = sum(acct.decode_kv_bytes(lens, win, D) for _, win in w.layers)
+    return {"workload": w.name, "ms_per_block_step": ms_block, "tokens_per_s": B / (ms_block * 1e-3),
+            "kv_bytes": kv, "kv_GBps": kv / (ms_block * 1e-3) / 1e9,
+            "note": "layers 2,3,5 re-read a buffer the previous layer just read (Infinity Cache may serve them)"}
+
+
+def bench_long(torch, m, acct, stream):
+    B, Hq, D, L = 8, 32, 128, 131072
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    bufs = make_decode_buffers(torch, m, B, L, D, 4, gen)
+    seq_lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    q = torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((B, Hq, D), device="cuda")
+    ws = m.decode_workspace(B, Hq, D, L, 0)
+
+    def calls():
+        for kv in bufs:
+            m.mqa_decode(q, kv, seq_lens, L, 0, out=out, workspace=ws)
+
+    with torch.cuda.stream(stream):
+        calls()
+        torch.cuda.synchronize()
+        reps = 25
+        ms, _ = run_steps(torch, calls, reps, True, stream)
+    ms_call = ms / (reps * len(bufs))
+    kv = acct.decode_kv_bytes([L] * B, 0, D)
+    return {"workload": "long_decode_B8_Hq32_D128_L131072", "us_per_call": ms_call * 1e3,
+            "tokens_per_s": B / (ms_call * 1e-3), "kv_GBps": kv / (ms_call * 1e-3) / 1e9,
+            "frac_hbm_peak": kv / (ms_call * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+
+def bench_prefill(torch, m, acct, stream):
+    B, C, P, Hq, D = 16, 512, 8192, 32, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    kv = make_decode_buffers(torch, m, B, P + C, D, 1, gen)[0]
+    q = torch.randn((B, C, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    plens = torch.full((B,), P, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, C, Hq, D), device="cuda")
+    res = {"workload": "prefill_B16_C512_P8192_Hq32_D128"}
+    with torch.cuda.stream(stream):
+        for win in (0, 1024):
+            def call():
+                m.mqa_prefill_chunk(q, kv, plens, P, win, out=out)
+            call()
+            torch.cuda.synchronize()
+            reps = 10
+            ms, _ = run_steps(torch, call, reps, True, stream)
+            ms_call = ms / reps
+            fl = acct.prefill_flops([P] * B, C, win, Hq, D)
+            tf = fl / (ms_call * 1e-3) / 1e12
+            res[f"W{win}"] = {"ms": ms_call, "flops": fl, "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS}
+    return res
+
+
+def cpu_baseline(budget_s: float):
+    """The oracle (numpy, float64) on a bounded sample of the decode workload.
+
+    Per sequence, the timed work is what one step does: encode the new token's
+    K and V rows, then the global and the window-1024 layer. The cache
+    contents are encoded beforehand, outside the timed region."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import oracle
+    import synth
+    B, Hq, D, L = 64, 32, 128, 4096
+    done, t_work = 0, 0.0
+    t_all = time.perf_counter()
+    while t_work < budget_s and done < B:
+        n = 4
+        k = synth.normal_f32(synth.rng(2, synth.T_K, 1000 + done), (n, L, D))
+        v = synth.normal_f32(synth.rng(2, synth.T_V, 1000 + done), (n, L, D))
+        q = synth.q_bf16(synth.rng(2, synth.T_Q, 1000 + done), (n, Hq, D))
+        lens = np.full(n, L, np.int32)
+        kq, ks = oracle.quantize_rows(k)
+        vq, vs = oracle.quantize_rows(v)
+        t0 = time.perf_counter()
+        kq[:, -1], ks[:, -1] = oracle.quantize_rows(k[:, -1])
+        vq[:, -1], vs[:, -1] = oracle.quantize_rows(v[:, -1])
+        for w in (0, 1024):
+            oracle.decode_ref(q, kq, ks, vq, vs, lens, w)
+        t_work += time.perf_counter() - t0
+        done += n
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    return {"value": done / t_work, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of the 64 sequences of one decode step (append + global layer + "
+                      f"window-1024 layer, 4096 keys, 32 heads, D=128); numpy float64 oracle, "
+                      f"{t_work:.1f} s of timed work",
+            "host_cpus": len(os.sched_getaffinity(0)), "wall_s": time.perf_counter() - t_all}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the decode path shards by sequence with no exchange, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import mqa_attention_int8_amd as m
+    from mqa_attention_int8_amd import accounting as acct
+    m.load_library()
+    torch.cuda.init()
+    stream = torch.cuda.Stream()
+    if args.copy_calibration:
+        x = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": x.numel() * 4, "copies": 3}), file=sys.stderr)
+    extra = {}
+    if args.only in (None, "decode"):
+        dec = bench_decode(torch, m, acct, args, stream)
+    else:
+        dec = None
+    if not args.no_extra:
+        if args.only in (None, "hybrid"):
+            extra["hybrid_block"] = bench_hybrid(torch, m, acct, stream)
+        if args.only in (None, "long"):
+            extra["long_context"] = bench_long(torch, m, acct, stream)
+        if args.only in (None, "prefill"):
+            extra["prefill"] = bench_prefill(torch, m, acct, stream)
+    if dec is None:
+        print(json.dumps({"extra": extra}))
+        return
+    cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
+    achieved = dec["global_GBps"]
+    line = {
+        "metric": METRIC, "value": dec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": dec["steps_done"], "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_B64_Hq32_D128_L4096: append + global layer + window-1024 layer "
+                               "sharing one int8 KV buffer",
+                   "B": 64, "Hq": 32, "D": 128, "seq_len": 4096, "windows": [0, 1024],
+                   "kv_rotation_copies": dec["rotation_copies"], "graph_replay": dec["graph"]},
+        "kv_read_GBps": dec["step_kv_GBps"], "kv_read_frac_hbm_peak": dec["step_kv_GBps"] / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "mqa_decode global layer (decode_partition_kernel + decode_merge_kernel)",
+                     "algorithmic_bytes_per_launch": dec["global_kv_bytes"],
+                     "avg_launch_us": dec["global_call_us"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * mqa_int8.h - C ABI of libmqa_int8.so: multi-query attention read from an
+ * int8 KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources are web pages; no code is taken from them):
+ *  - Multi-query attention: all query heads of a layer share ONE K/V head.
+ *    [9c1h.cn news page on Character.AI's inference optimizations, section
+ *    "秘訣1", MQA item; explinks.com page "Character.AI 的最佳实践", section
+ *    "多查询注意力".]
+ *  - Local layers attend to a sliding window of the most recent keys (1024 in
+ *    production), global layers to all keys. [9c1h.cn page, "秘訣1", hybrid
+ *    attention horizon item; explinks.com page, "混合注意力范围".]
+ *  - Adjacent layers may share one KV cache. [9c1h.cn page, "秘訣1",
+ *    cross-layer KV sharing item; explinks.com page, "跨层 KV 共享".] Here a
+ *    shared cache is one mqa_kv_view passed to several calls; attention calls
+ *    only read it.
+ *  - The KV cache is int8. [explinks.com page, "训练和服务的量化".] The pages
+ *    do not fix the scheme; this library uses one fp32 scale per token row,
+ *    scale = fl32(absmax / 127), code = clamp(rint(x / scale), -127, 127)
+ *    with correctly rounded fp32 division and ties to even.
+ *  - Decode (one new token per sequence) is bound by HBM reads of the cache;
+ *    prefill is bound by arithmetic. [tubrief.io LLM-inference workshop
+ *    transcript, 00:20:54-00:26:30; devpress.csdn.net article on the Chitu
+ *    engine, section 1.1.]
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, in
+ *    row-major, contiguous layout as stated per argument. The caller owns all
+ *    memory; the library never allocates, frees or retains pointers.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on that stream and returns; the return code reports
+ *    argument validation and launch errors only (MQA_ERR_HIP for a failed
+ *    launch). Errors inside kernels surface on the stream, as with any HIP
+ *    kernel.
+ *  - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *  - Device-resident lengths (seq_lens, prefix_lens, start_pos) are trusted
+ *    data: kernels clamp them into the cache so that no access leaves the
+ *    buffers, but results for out-of-range values are unspecified.
+ *  - Supported shapes: head_dim D in {64, 128}; 1 <= Hq <= 64 query heads;
+ *    B >= 1. Validation happens before any HIP call, so bad arguments are
+ *    reported without touching the device.
+ */
+#ifndef MQA_INT8_H
+#define MQA_INT8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MQA_OK = 0,
+  MQA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  MQA_ERR_SHAPE = 2,       /* a size is out of range (<= 0, or inconsistent)    */
+  MQA_ERR_UNSUPPORTED = 3, /* a shape this build does not implement (D, Hq)     */
+  MQA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                  */
+  MQA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
+  MQA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed        */
+} mqa_status;
+
+/* Non-owning description of ONE shared KV buffer (one K/V head per token).
+ * k, v: int8 [B, L_cap, D]; k_scale, v_scale: fp32 [B, L_cap] (one scale per
+ * token row). Several layers may pass the same view (cross-layer sharing).
+ * The struct itself lives in HOST memory and is read only during the call. */
+typedef struct {
+  const int8_t* k;
+  const int8_t* v;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t L_cap;
+} mqa_kv_view;
+
+/* kv_quantize_int8 - write T new token rows per sequence into an int8 cache.
+ * [explinks.com page "Character.AI 的最佳实践", "训练和服务的量化": int8 KV.]
+ *   src        fp32 [B, T, D], the new K (or V) rows.
+ *   dst        int8 [B, L_cap, D]; rows start_pos[b] .. start_pos[b]+T-1 of
+ *              sequence b are written, nothing else.
+ *   dst_scale  fp32 [B, L_cap]; the same rows' scales are written.
+ *   start_pos  int32 [B] (device): first row written for each sequence.
+ *              Rows that would fall outside [0, L_cap) are skipped.
+ * Encoding per row x: a = max|x|; s = fl32(a/127); s == 0 gives an all-zero
+ * row with scale 0; otherwise q = clamp(rint(fl32(x/s)), -127, 127).
+ * Call once for K and once for V. Errors: NULL, SHAPE (B,T<=0, L_cap<T),
+ * UNSUPPORTED (D not 64/128), ALIGN (src/dst not 16-byte aligned), HIP. */
+int kv_quantize_int8(const float* src, int8_t* dst, float* dst_scale,
+                     const int32_t* start_pos, int32_t B, int32_t T, int32_t D,
+                     int32_t L_cap, void* stream);
+
+/* Bytes of device workspace mqa_decode needs for these arguments (0 when the
+ * call runs as a single pass). Pure host function; it may query the current
+ * device's compute-unit count and assumes 256 when there is no device. */
+size_t mqa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
+                                  int32_t max_seq_len, int32_t window);
+
+/* mqa_decode - one decode step of one attention layer.
+ * [9c1h.cn page "秘訣1" (MQA, sliding window, KV sharing); workshop transcript
+ * 00:48:02-00:49:13 (tiled attention with an online softmax).]
+ *   q            bf16 [B, Hq, D]: the new token's query heads.
+ *   kv           host pointer to the layer's KV view (may be shared).
+ *   seq_lens     int32 [B] (device): keys per sequence INCLUDING the new
+ *                token, which the caller has already written to the cache.
+ *   max_seq_len  host upper bound of seq_lens (sizes the launch).
+ *   window       > 0: attend to the last `window` keys (including the new
+ *                token); <= 0: global.
+ *   softmax_scale  multiplies q.k before the softmax (usually 1/sqrt(D)).
+ *   out          fp32 [B, Hq, D]. A sequence with no visible key gets zeros.
+ *   workspace    device scratch of at least mqa_decode_workspace_bytes()
+ *                bytes (may be NULL when that is 0). Its contents need no
+ *                initialisation and are overwritten; it may be reused by any
+ *                later call it is large enough for. Calls that may run
+ *                concurrently must not share a workspace.
+ * Long or many-partition contexts are split into key ranges whose partial
+ * softmax states are combined by a log-sum-exp merge (exact up to rounding).
+ * Layout requirements: q, k, v, out and workspace 16-byte aligned; k_scale
+ * and v_scale 16-byte aligned with L_cap a multiple of 4 (scales are read
+ * four keys at a time).
+ * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, WORKSPACE, HIP. */
+int mqa_decode(const uint16_t* q, const mqa_kv_view* kv,
+               const int32_t* seq_lens, int32_t max_seq_len, int32_t B,
+               int32_t Hq, int32_t D, int32_t window, float softmax_scale,
+               float* out, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* mqa_prefill_chunk - attention of a new chunk of C tokens per sequence over
+ * a cached prefix plus the chunk itself (causal).
+ * [9c1h.cn page "秘訣2" (cached prefixes reused across turns); workshop
+ * transcript 00:20:54-00:22:12 (prefill is the compute-bound phase).]
+ *   q            bf16 [B, C, Hq, D].
+ *   kv           host pointer to the KV view; the chunk's own K/V must
+ *                already be in the cache at rows prefix_lens[b] ..
+ *                prefix_lens[b]+C-1 (written with kv_quantize_int8).
+ *   prefix_lens  int32 [B] (device): cached tokens before the chunk.
+ *   max_prefix_len host upper bound of prefix_lens.
+ *   window       > 0: query at absolute position p sees keys
+ *                max(0, p-window+1) .. p; <= 0: keys 0 .. p.
+ *   out          fp32 [B, C, Hq, D].
+ * Errors: NULL, SHAPE (C<=0, max_prefix_len+C > L_cap, ...), UNSUPPORTED,
+ * ALIGN, HIP. */
+int mqa_prefill_chunk(const uint16_t* q, const mqa_kv_view* kv,
+                      const int32_t* prefix_lens, int32_t max_prefix_len,
+                      int32_t B, int32_t C, int32_t Hq, int32_t D,
+                      int32_t window, float softmax_scale, float* out,
+                      void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* mqa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQA_INT8_H */

@@ -1,0 +1,216 @@
+"""Thin Python binding of libmqa_int8.so (argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of its own: shapes and dtypes are checked, raw device pointers and
+torch's current HIP stream are handed to the library, and a non-zero status
+raises ``MQAError``. PyTorch is used for device memory and streams only.
+
+The library must be built (``python -m mqa_attention_int8_amd.build``); a
+missing library raises at first use - there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmqa_int8.so")
+_lock = threading.Lock()
+_lib = None
+
+MQA_OK = 0
+
+
+class MQAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = int(code)
+        super().__init__(f"{where}: status {code}: {mqa_status_string(code)}")
+
+
+class mqa_kv_view(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("L_cap", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmqa_int8.so once (after torch, so both share one HIP runtime)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is not built; run python -m mqa_attention_int8_amd.build")
+        lib = ctypes.CDLL(_LIB_PATH)
+        i32, vp, f32 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+        lib.mqa_status_string.argtypes = [ctypes.c_int]
+        lib.mqa_status_string.restype = ctypes.c_char_p
+        lib.kv_quantize_int8.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp]
+        lib.kv_quantize_int8.restype = ctypes.c_int
+        lib.mqa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.mqa_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.mqa_decode.argtypes = [vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32, f32,
+                                   vp, vp, ctypes.c_size_t, vp]
+        lib.mqa_decode.restype = ctypes.c_int
+        lib.mqa_prefill_chunk.argtypes = [vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32,
+                                          i32, f32, vp, vp]
+        lib.mqa_prefill_chunk.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def mqa_status_string(code: int) -> str:
+    return load_library().mqa_status_string(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != MQA_OK:
+        raise MQAError(code, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class KVView:
+    """One KV buffer: int8 K/V [B, L_cap, D] and fp32 scales [B, L_cap].
+
+    Several layers may hold the same KVView (cross-layer KV sharing)."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor):
+        for t, n in ((k, "k"), (v, "v")):
+            _need(t, torch.int8, n, 3)
+        for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            _need(t, torch.float32, n, 2)
+        if k.shape != v.shape or k_scale.shape != v_scale.shape or tuple(k.shape[:2]) != tuple(k_scale.shape):
+            raise ValueError("inconsistent KV buffer shapes")
+        self.k, self.v, self.k_scale, self.v_scale = k, v, k_scale, v_scale
+        self.B, self.L_cap, self.D = (int(x) for x in k.shape)
+
+    @classmethod
+    def empty(cls, B: int, L_cap: int, D: int, device="cuda"):
+        return cls(torch.empty((B, L_cap, D), dtype=torch.int8, device=device),
+                   torch.empty((B, L_cap, D), dtype=torch.int8, device=device),
+                   torch.zeros((B, L_cap), dtype=torch.float32, device=device),
+                   torch.zeros((B, L_cap), dtype=torch.float32, device=device))
+
+    def c_view(self) -> mqa_kv_view:
+        return mqa_kv_view(self.k.data_ptr(), self.v.data_ptr(), self.k_scale.data_ptr(),
+                           self.v_scale.data_ptr(), self.L_cap)
+
+
+def kv_quantize_int8(src: torch.Tensor, dst: torch.Tensor, dst_scale: torch.Tensor,
+                     start_pos: torch.Tensor, stream=None) -> None:
+    """Quantize src fp32 [B, T, D] into rows start_pos[b].. of dst / dst_scale."""
+    lib = load_library()
+    _need(src, torch.float32, "src", 3)
+    _need(dst, torch.int8, "dst", 3)
+    _need(dst_scale, torch.float32, "dst_scale", 2)
+    _need(start_pos, torch.int32, "start_pos", 1)
+    B, T, D = (int(x) for x in src.shape)
+    if dst.shape[0] != B or dst.shape[2] != D or tuple(dst_scale.shape) != tuple(dst.shape[:2]) \
+            or start_pos.shape[0] != B:
+        raise ValueError("kv_quantize_int8: shape mismatch")
+    _check(lib.kv_quantize_int8(_ptr(src), _ptr(dst), _ptr(dst_scale), _ptr(start_pos), B, T, D,
+                                int(dst.shape[1]), _stream(stream)), "kv_quantize_int8")
+
+
+def append_kv(kv: KVView, k_new: torch.Tensor, v_new: torch.Tensor, start_pos: torch.Tensor,
+              stream=None) -> None:
+    """Write new K and V rows (fp32 [B, T, D]) into a KV buffer: two kv_quantize_int8 calls."""
+    kv_quantize_int8(k_new, kv.k, kv.k_scale, start_pos, stream)
+    kv_quantize_int8(v_new, kv.v, kv.v_scale, start_pos, stream)
+
+
+def mqa_decode_workspace_bytes(B: int, Hq: int, D: int, max_seq_len: int, window: int) -> int:
+    return int(load_library().mqa_decode_workspace_bytes(B, Hq, D, max_seq_len, window))
+
+
+def decode_workspace(B: int, Hq: int, D: int, max_seq_len: int, window: int, device="cuda"):
+    """A workspace for mqa_decode (None when none is needed); reusable by any
+    later call on the same stream that it is large enough for."""
+    need = mqa_decode_workspace_bytes(B, Hq, D, max_seq_len, window)
+    if need == 0:
+        return None
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+def default_softmax_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def mqa_decode(q: torch.Tensor, kv: KVView, seq_lens: torch.Tensor, max_seq_len: int, window: int,
+               softmax_scale: float | None = None, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode step: q bf16 [B, Hq, D] -> out fp32 [B, Hq, D]."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q", 3)
+    _need(seq_lens, torch.int32, "seq_lens", 1)
+    B, Hq, D = (int(x) for x in q.shape)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out", 3)
+    need = mqa_decode_workspace_bytes(B, Hq, D, max_seq_len, window)
+    if workspace is None and need > 0:
+        workspace = decode_workspace(B, Hq, D, max_seq_len, window, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
+    view = kv.c_view()
+    _check(lib.mqa_decode(_ptr(q), ctypes.byref(view), _ptr(seq_lens), int(max_seq_len), B, Hq, D,
+                          int(window), scale, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
+           "mqa_decode")
+    return out
+
+
+def mqa_prefill_chunk(q: torch.Tensor, kv: KVView, prefix_lens: torch.Tensor, max_prefix_len: int,
+                      window: int, softmax_scale: float | None = None,
+                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Causal chunk attention: q bf16 [B, C, Hq, D] -> out fp32 [B, C, Hq, D]."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q", 4)
+    _need(prefix_lens, torch.int32, "prefix_lens", 1)
+    B, C, Hq, D = (int(x) for x in q.shape)
+    if out is None:
+        out = torch.empty((B, C, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out", 4)
+    scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
+    view = kv.c_view()
+    _check(lib.mqa_prefill_chunk(_ptr(q), ctypes.byref(view), _ptr(prefix_lens), int(max_prefix_len), B,
+                                 C, Hq, D, int(window), scale, _ptr(out), _stream(stream)),
+           "mqa_prefill_chunk")
+    return out
+
+
+def hip_runtimes_mapped() -> list[str]:
+    """Paths of the HIP runtime libraries mapped into this process (diagnostic)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for ln in f:
+            if "libamdhip64" in ln:
+                paths.add(ln.split()[-1])
+    return sorted(paths)

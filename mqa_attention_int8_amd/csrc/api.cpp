@@ -1,0 +1,126 @@
+// C ABI of libmqa_int8: argument validation and dispatch.
+//
+// Validation runs before any HIP call, so invalid arguments are reported on a
+// machine without a GPU. The library keeps no state except the cached
+// compute-unit count of each device it has seen.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "../../include/mqa_int8.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (cached > 0) return cached;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool supported_d(int32_t D) { return D == 64 || D == 128; }
+bool supported_hq(int32_t Hq) { return Hq >= 1 && Hq <= 64; }
+
+int check_kv(const mqa_kv_view* kv, int32_t D) {
+  if (!kv || !kv->k || !kv->v || !kv->k_scale || !kv->v_scale) return MQA_ERR_NULL;
+  if (kv->L_cap <= 0) return MQA_ERR_SHAPE;
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return MQA_ERR_ALIGN;
+  if (((uintptr_t)kv->k_scale & 3u) || ((uintptr_t)kv->v_scale & 3u)) return MQA_ERR_ALIGN;
+  (void)D;
+  return MQA_OK;
+}
+
+// Validation of mqa_decode's arguments (shared with the workspace query).
+int check_decode_shape(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || max_seq_len < 0) return MQA_ERR_SHAPE;
+  if (!supported_d(D) || !supported_hq(Hq)) return MQA_ERR_UNSUPPORTED;
+  if ((int64_t)B > 65535) return MQA_ERR_SHAPE;  // grid.y limit
+  return MQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mqa_status_string(int status) {
+  switch (status) {
+    case MQA_OK: return "ok";
+    case MQA_ERR_NULL: return "a required pointer is NULL";
+    case MQA_ERR_SHAPE: return "a size argument is out of range or inconsistent";
+    case MQA_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be 64 or 128, 1 <= Hq <= 64)";
+    case MQA_ERR_ALIGN: return "a pointer is not suitably aligned (16 bytes for tensors, 4 for scales)";
+    case MQA_ERR_WORKSPACE: return "workspace is missing or smaller than mqa_decode_workspace_bytes()";
+    case MQA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int kv_quantize_int8(const float* src, int8_t* dst, float* dst_scale, const int32_t* start_pos,
+                     int32_t B, int32_t T, int32_t D, int32_t L_cap, void* stream) {
+  if (!src || !dst || !dst_scale || !start_pos) return MQA_ERR_NULL;
+  if (B <= 0 || T <= 0 || D <= 0 || L_cap <= 0 || L_cap < T) return MQA_ERR_SHAPE;
+  if (!supported_d(D)) return MQA_ERR_UNSUPPORTED;
+  if (!aligned16(src) || !aligned16(dst) || ((uintptr_t)dst_scale & 3u)) return MQA_ERR_ALIGN;
+  return mqa::launch_quantize(src, dst, dst_scale, start_pos, B, T, D, L_cap,
+                              static_cast<hipStream_t>(stream));
+}
+
+size_t mqa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len,
+                                  int32_t window) {
+  if (check_decode_shape(B, Hq, D, max_seq_len) != MQA_OK) return 0;
+  return mqa::plan_decode(B, Hq, D, max_seq_len, window, device_cu_count()).ws_bytes;
+}
+
+int mqa_decode(const uint16_t* q, const mqa_kv_view* kv, const int32_t* seq_lens,
+               int32_t max_seq_len, int32_t B, int32_t Hq, int32_t D, int32_t window,
+               float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  if (!q || !kv || !seq_lens || !out) return MQA_ERR_NULL;
+  int st = check_decode_shape(B, Hq, D, max_seq_len);
+  if (st != MQA_OK) return st;
+  st = check_kv(kv, D);
+  if (st != MQA_OK) return st;
+  if (max_seq_len > kv->L_cap) return MQA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(out)) return MQA_ERR_ALIGN;
+  // scales are read four keys at a time
+  if ((kv->L_cap & 3) || !aligned16(kv->k_scale) || !aligned16(kv->v_scale)) return MQA_ERR_ALIGN;
+  const mqa::DecodePlan plan = mqa::plan_decode(B, Hq, D, max_seq_len, window, device_cu_count());
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+  }
+  return mqa::launch_decode(q, *kv, seq_lens, B, Hq, D, window, softmax_scale, out, workspace, plan,
+                            static_cast<hipStream_t>(stream));
+}
+
+int mqa_prefill_chunk(const uint16_t* q, const mqa_kv_view* kv, const int32_t* prefix_lens,
+                      int32_t max_prefix_len, int32_t B, int32_t C, int32_t Hq, int32_t D,
+                      int32_t window, float softmax_scale, float* out, void* stream) {
+  if (!q || !kv || !prefix_lens || !out) return MQA_ERR_NULL;
+  if (B <= 0 || C <= 0 || Hq <= 0 || D <= 0 || max_prefix_len < 0) return MQA_ERR_SHAPE;
+  if (!supported_d(D) || !supported_hq(Hq)) return MQA_ERR_UNSUPPORTED;
+  int st = check_kv(kv, D);
+  if (st != MQA_OK) return st;
+  if ((int64_t)max_prefix_len + C > kv->L_cap) return MQA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(out)) return MQA_ERR_ALIGN;
+  return mqa::launch_prefill(q, *kv, prefix_lens, max_prefix_len, B, C, Hq, D, window,
+                             softmax_scale, out, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Device-side helpers shared by the kernels of libmqa_int8 (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// v_mfma_f32_16x16x32_bf16. Lane l = 16*g + c (g = l/16, c = l%16):
+//   A (16x32, M x K): lane holds A[c][8g .. 8g+7]
+//   B (32x16, K x N): lane holds B[8g .. 8g+7][c]
+//   C (16x16, M x N): lane holds C[4g + r][c], r = 0..3
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
+
+// Pack the bf16 patterns of two fp32 values whose low 16 bits are zero (for
+// example small integers): result = hi16(b) << 16 | hi16(a).
+__device__ __forceinline__ uint32_t pack_hi16(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// Four int8 codes (one 32-bit word) -> four exact bf16 values, as two words.
+// Every int8 value (including -128) has at most 8 significant bits, so the
+// fp32 conversion is exact and its upper half is the exact bf16 pattern.
+// (float)(signed char)(w >> 8k) is a single v_cvt_f32_i32 with an SDWA
+// sign-extended byte select on gfx950.
+__device__ __forceinline__ u32x2 i8x4_to_bf16(uint32_t w) {
+  const float f0 = (float)(signed char)(w);
+  const float f1 = (float)(signed char)(w >> 8);
+  const float f2 = (float)(signed char)(w >> 16);
+  const float f3 = (float)(signed char)(w >> 24);
+  return u32x2{pack_hi16(f0, f1), pack_hi16(f2, f3)};
+}
+
+// Byte `sel` (0..3) of a word as an exact fp32 value of the signed int8.
+__device__ __forceinline__ float i8_byte(uint32_t w, int sel) {
+  return (float)(signed char)(w >> (8 * sel));
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Split two fp32 values into bf16 hi + lo parts, both rounded to nearest
+// even: x = hi + lo + e with |e| <= 2^-18 |x| (hi keeps 8 significant bits,
+// the exact fp32 remainder x - hi is rounded to 8 more). Returns {hi, lo}
+// as packed pairs.
+__device__ __forceinline__ u32x2 split_bf16(float a, float b) {
+  const uint32_t h = cvt_pk_bf16(a, b);
+  return u32x2{h, cvt_pk_bf16(a - bf16_lo_to_f32(h), b - bf16_hi_to_f32(h))};
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (v_permlane{16,32}_swap).
+__device__ __forceinline__ float quad_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 2^x with the hardware instruction (no denormal range handling: results
+// below the normal range flush to 0, which only drops negligible weights).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer resource over [base, base + bytes): loads beyond it return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+}  // namespace mqa

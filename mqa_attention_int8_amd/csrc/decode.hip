@@ -1,0 +1,542 @@
+// mqa_decode: one decode step of multi-query attention over an int8 KV cache.
+//
+// What is computed (9c1h.cn news page on Character.AI's inference tricks,
+// section 秘訣1; explinks.com "Character.AI 的最佳实践", sections 多查询注意力,
+// 混合注意力范围, 跨层 KV 共享, 训练和服务的量化): for every sequence b and
+// query head h,
+//     z_j = scale * s_k[j] * (q_h . k_j)             j in the visible keys
+//     out_h = sum_j softmax(z)_j * s_v[j] * v_j
+// where k_j, v_j are int8 rows of the ONE shared KV head and the visible keys
+// are [max(0, n-W), n) for a window W > 0, else [0, n).
+//
+// Design for gfx950 (decode is bound by HBM reads of the cache):
+//  * One work-group = one sequence x one contiguous range of 32-key tiles
+//    (a "partition"), ALL query heads. Each K/V byte is read from HBM once
+//    per call and feeds every head: this is where MQA's reuse lives.
+//  * Per 32-key tile a wave runs S^T = K Q^T and O^T += V^T P'^T on bf16
+//    MFMA (v_mfma_f32_16x16x32_bf16): 32 heads x 128 dims x 2 flops per key
+//    per product is far above what the vector ALUs can sustain at HBM rate.
+//  * int8 -> bf16 is exact and costs one instruction per element (an SDWA
+//    sign-extended byte convert) plus one permute per pair.
+//  * The contraction index d is permuted consistently in Q and K so that a
+//    lane's K bytes are one contiguous run of a key row; the key index is
+//    permuted consistently in P' and V so that the accumulator layout of S^T
+//    is directly the B operand of the PV product (no shuffles), and V's
+//    column mapping makes each lane's V bytes contiguous within a row.
+//  * P' = p * s_v is split into bf16 hi + lo parts (two MFMAs), so the PV
+//    product carries ~16 significant bits instead of 8.
+//  * Loads are software-pipelined: the next tile's K, V and scales are in
+//    flight while the current tile is computed.
+//  * Online softmax (running max m, sum l, rescaled accumulator) in the log2
+//    domain per head, rescaling only when the max grows by more than 2^8.
+//    The 4 waves of a work-group merge through LDS. With several partitions
+//    per sequence, each work-group writes its (m, l, o) state and a small
+//    second kernel combines them with a log-sum-exp merge (workshop
+//    transcript 00:48:02-00:49:13: tiles plus three running quantities give
+//    the exact softmax). A kernel boundary is the cheap way to make the
+//    states written on one XCD visible to another; an in-kernel hand-off
+//    needs an L2 write-back per work-group.
+//  * Tiles wholly outside the window are never loaded; only the tiles that
+//    straddle a window end are masked per key.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace mqa {
+
+namespace {
+
+constexpr int kTileKeys = 32;
+constexpr int kWaves = 4;
+constexpr float kLazy = 8.0f;  // rescale only when the running max grows by > 2^8
+
+struct DecodeParams {
+  const uint16_t* q;
+  const int8_t* k;
+  const int8_t* v;
+  const float* ks;
+  const float* vs;
+  const int32_t* seq_lens;
+  float* out;
+  float* ws_o;       // [B, P, Hq, D] partial accumulators (natural d order)
+  float2* ws_ml;     // [B, P, Hq] (max in log2 units, sum)
+  int32_t L_cap;
+  int32_t Hq;
+  int32_t window;
+  int32_t tiles_per_part;
+  int32_t num_parts;
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+// Raw bytes of one 32-key tile as one lane needs them.
+template <int D>
+struct Tile {
+  static constexpr int KV4 = D / 64;  // 16-byte K chunks per lane per 16 keys
+  static constexpr int VW = D / 64;   // V words per lane per key
+  u32x4 k[2][KV4];
+  uint32_t v[8][VW];
+  f32x4 ks[2];
+  f32x4 vs[2];
+};
+
+// Per-lane constant byte offsets of a tile's loads (the tile base enters as
+// the wave-uniform scalar offset, so the hot loop has no address arithmetic).
+struct TileOffsets {
+  uint32_t k;   // key base+c, bytes [g*D/4, (g+1)*D/4)
+  uint32_t v;   // key base+4g, bytes [D/16*c, D/16*(c+1))
+  uint32_t s;   // scales of keys base+4g .. base+4g+3
+};
+
+struct SeqBuffers {
+  __amdgpu_buffer_rsrc_t k, v, ks, vs;
+};
+
+// Loads are issued unconditionally so the compiler can count them (a load
+// under a runtime branch makes it wait for every outstanding load); a tile
+// that does not exist is pointed past the buffer ends, where buffer loads
+// return zero without a memory access.
+constexpr uint32_t kNowhere = 0x80000000u;
+
+template <int D>
+__device__ __forceinline__ void load_tile(Tile<D>& t, const SeqBuffers& sb, const TileOffsets& off0,
+                                          int base, bool exists) {
+  TileOffsets off = off0;
+  if (!exists) {
+    off.k = kNowhere;
+    off.v = kNowhere;
+    off.s = kNowhere;
+    base = 0;
+  }
+  // scalar offsets of the tile's first row (base is wave-uniform)
+  const uint32_t kv_s = __builtin_amdgcn_readfirstlane((uint32_t)base * D);
+  const uint32_t sc_s = __builtin_amdgcn_readfirstlane((uint32_t)base * 4);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int w = 0; w < Tile<D>::KV4; ++w) t.k[hf][w] = buf_load16(sb.k, off.k + hf * 16 * D + 16 * w, kv_s);
+  // key slot i: key base + 16(i/4) + 4g + i%4
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t o = off.v + (16 * (i >> 2) + (i & 3)) * D;
+    if constexpr (Tile<D>::VW == 2) {
+      const u32x2 x = buf_load8(sb.v, o, kv_s);
+      t.v[i][0] = x[0];
+      t.v[i][1] = x[1];
+    } else {
+      t.v[i][0] = buf_load4(sb.v, o, kv_s);
+    }
+  }
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    t.ks[hf] = __builtin_bit_cast(f32x4, buf_load16(sb.ks, off.s + 64 * hf, sc_s));
+    t.vs[hf] = __builtin_bit_cast(f32x4, buf_load16(sb.vs, off.s + 64 * hf, sc_s));
+  }
+}
+
+// Running state of one wave: online-softmax quantities of its NT*16 heads.
+template <int D, int NT>
+struct WaveState {
+  f32x4 oacc[D / 16][NT];
+  float m_run[NT];
+  float l_run[NT];
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
+                                             const bf16x8 (&qop)[NT][D / 32],
+                                             float scale_log2, int base, int lo, int hi, int g) {
+  constexpr int KK = D / 32;
+  constexpr int DPL = D / 16;
+  const bool interior = (base >= lo) && (base + kTileKeys <= hi);
+
+  // ---- S^T = K Q^T ---------------------------------------------------------
+  f32x4 s[2][NT];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) s[hf][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4 w = cur.k[hf][kk >> 1];
+      const bf16x8 kop =
+          as_bf16x8(cat(i8x4_to_bf16(w[2 * (kk & 1)]), i8x4_to_bf16(w[2 * (kk & 1) + 1])));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) s[hf][nt] = mfma16(kop, qop[nt][kk], s[hf][nt]);
+    }
+  }
+
+  // ---- online softmax (log2 domain); P' = p * s_v as bf16 hi + lo ----------
+  float kscl[8], vscl[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kscl[i] = cur.ks[0][i] * scale_log2;
+    kscl[4 + i] = cur.ks[1][i] * scale_log2;
+    vscl[i] = cur.vs[0][i];
+    vscl[4 + i] = cur.vs[1][i];
+  }
+  bool ok[8];
+  if (!interior) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = base + 16 * (i >> 2) + 4 * g + (i & 3);
+      ok[i] = (j >= lo) && (j < hi);
+      vscl[i] = ok[i] ? vscl[i] : 0.f;
+    }
+  }
+  bf16x8 phi[NT], plo[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float z[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = s[i >> 2][nt][i & 3] * kscl[i];
+    if (!interior) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] = ok[i] ? z[i] : -INFINITY;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                       fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+    tmax = quad_max(tmax);
+    if (__builtin_amdgcn_ballot_w64(tmax > st.m_run[nt] + kLazy) != 0) {
+      const float m_new = fmaxf(st.m_run[nt], tmax);
+      const float alpha = fast_exp2(st.m_run[nt] - m_new);   // 0 when m_run = -inf
+      st.m_run[nt] = m_new;
+      st.l_run[nt] *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < DPL; ++mt) st.oacc[mt][nt] *= alpha;
+    }
+    const float m_use = st.m_run[nt];
+    u32x4 hw, lw;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float e0 = fast_exp2(z[i] - m_use);
+      const float e1 = fast_exp2(z[i + 1] - m_use);
+      st.l_run[nt] += e0 + e1;
+      const u32x2 hl = split_bf16(e0 * vscl[i], e1 * vscl[i + 1]);
+      hw[i >> 1] = hl[0];
+      lw[i >> 1] = hl[1];
+    }
+    phi[nt] = as_bf16x8(hw);
+    plo[nt] = as_bf16x8(lw);
+  }
+
+  // ---- O^T += V^T P'^T -------------------------------------------------------
+#pragma unroll
+  for (int mt = 0; mt < DPL; ++mt) {
+    u32x4 a;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2)
+      a[i >> 1] = pack_hi16(i8_byte(cur.v[i][mt >> 2], mt & 3), i8_byte(cur.v[i + 1][mt >> 2], mt & 3));
+    const bf16x8 vop = as_bf16x8(a);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      st.oacc[mt][nt] = mfma16(vop, phi[nt], st.oacc[mt][nt]);
+      st.oacc[mt][nt] = mfma16(vop, plo[nt], st.oacc[mt][nt]);
+    }
+  }
+}
+
+template <int D, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2 : 1))) void decode_partition_kernel(DecodeParams p) {
+  constexpr int KK = D / 32;   // MFMAs along d per 16 keys
+  constexpr int DPL = D / 16;  // PV m-tiles; V bytes per lane per key
+  constexpr int HP = NT * 16;  // padded head count
+  constexpr int OSTR = D + 4;  // LDS row stride of the merged accumulator
+
+  // merged accumulator, per head: column mt*16 + m holds d = DPL*m + mt
+  __shared__ __attribute__((aligned(16))) float sm_o[HP * OSTR];
+  __shared__ float sm_m[kWaves][HP];
+  __shared__ float sm_l[kWaves][HP];
+  __shared__ float sm_M[HP];
+  __shared__ float sm_L[HP];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const int b = blockIdx.y;
+  const int part = blockIdx.x;
+  const int Hq = p.Hq;
+
+  int n = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);  // same for the whole work-group
+  n = n < 0 ? 0 : (n > p.L_cap ? p.L_cap : n);
+  const int lo = p.window > 0 ? max(0, n - p.window) : 0;
+  const int hi = n;
+  const int t_begin = lo / kTileKeys;
+  const int t_end = hi > lo ? (hi + kTileKeys - 1) / kTileKeys : t_begin;
+  const int pt0 = t_begin + part * p.tiles_per_part;
+  const int pt1 = min(pt0 + p.tiles_per_part, t_end);
+
+  // One buffer resource per tensor of this sequence; loads past the cache
+  // capacity return zero (rows past the valid keys are masked anyway).
+  SeqBuffers sb;
+  sb.k = make_rsrc(p.k + (int64_t)b * p.L_cap * D, (uint32_t)p.L_cap * D);
+  sb.v = make_rsrc(p.v + (int64_t)b * p.L_cap * D, (uint32_t)p.L_cap * D);
+  sb.ks = make_rsrc(p.ks + (int64_t)b * p.L_cap, (uint32_t)p.L_cap * 4);
+  sb.vs = make_rsrc(p.vs + (int64_t)b * p.L_cap, (uint32_t)p.L_cap * 4);
+  TileOffsets off;
+  off.k = (uint32_t)(c * D + g * (D / 4));
+  off.v = (uint32_t)(4 * g * D + (D / 16) * c);
+  off.s = (uint32_t)(16 * g);
+
+  // First tile's loads go out before anything else.
+  Tile<D> ta, tb;
+  int t = pt0 + wave;
+  load_tile<D>(ta, sb, off, t * kTileKeys, t < pt1);
+
+  // Q^T as the B operand: lane holds q[h = 16nt + c][d = g*D/4 + 8kk + 0..7].
+  bf16x8 qop[NT][KK];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int h = 16 * nt + c;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (h < Hq)
+        w = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)b * Hq + h) * D + g * (D / 4) + 8 * kk);
+      qop[nt][kk] = as_bf16x8(w);
+    }
+  }
+
+  WaveState<D, NT> st;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    st.m_run[nt] = -INFINITY;
+    st.l_run[nt] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < DPL; ++mt) st.oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Two tiles in registers, used alternately: one computing, one in flight.
+  while (t < pt1) {
+    load_tile<D>(tb, sb, off, (t + kWaves) * kTileKeys, t + kWaves < pt1);
+    compute_tile<D, NT>(ta, st, qop, p.scale_log2, t * kTileKeys, lo, hi, g);
+    t += kWaves;
+    if (t >= pt1) break;
+    load_tile<D>(ta, sb, off, (t + kWaves) * kTileKeys, t + kWaves < pt1);
+    compute_tile<D, NT>(tb, st, qop, p.scale_log2, t * kTileKeys, lo, hi, g);
+    t += kWaves;
+  }
+
+  // ---- merge the 4 waves of the work-group --------------------------------
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    st.l_run[nt] = quad_sum(st.l_run[nt]);
+    if (g == 0) {
+      sm_m[wave][16 * nt + c] = st.m_run[nt];
+      sm_l[wave][16 * nt + c] = st.l_run[nt];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < HP) {
+    const int h = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    float L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (sm_m[w][h] != -INFINITY) L += sm_l[w][h] * exp2f(sm_m[w][h] - M);
+    }
+    sm_M[h] = M;
+    sm_L[h] = L;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float M = sm_M[16 * nt + c];
+    const float f = (st.m_run[nt] == -INFINITY) ? 0.f : exp2f(st.m_run[nt] - M);
+#pragma unroll
+    for (int mt = 0; mt < DPL; ++mt) st.oacc[mt][nt] *= f;
+  }
+  // Deterministic accumulation: wave 0 stores, waves 1..3 add in order.
+  for (int w = 0; w < kWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int mt = 0; mt < DPL; ++mt) {
+          f32x4* dst = reinterpret_cast<f32x4*>(&sm_o[(16 * nt + c) * OSTR + 16 * mt + 4 * g]);
+          *dst = (w == 0) ? st.oacc[mt][nt] : *dst + st.oacc[mt][nt];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- single partition: normalise and write ---------------------------
+  constexpr int D4 = D / 4;
+  if (p.num_parts == 1) {
+    for (int e = threadIdx.x; e < Hq * D4; e += 256) {
+      const int h = e / D4, d0 = 4 * (e % D4);
+      const float L = sm_L[h];
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      f32x4 o;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int d = d0 + u;
+        o[u] = sm_o[h * OSTR + 16 * (d % DPL) + d / DPL] * inv;
+      }
+      *reinterpret_cast<f32x4*>(p.out + ((int64_t)b * Hq + h) * D + d0) = o;
+    }
+    return;
+  }
+
+  // ---- several partitions: publish this partition's state ------------------
+  const int64_t slot = (int64_t)b * p.num_parts + part;
+  for (int e = threadIdx.x; e < Hq * D4; e += 256) {
+    const int h = e / D4, d0 = 4 * (e % D4);
+    f32x4 o;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = d0 + u;
+      o[u] = sm_o[h * OSTR + 16 * (d % DPL) + d / DPL];
+    }
+    *reinterpret_cast<f32x4*>(p.ws_o + (slot * Hq + h) * D + d0) = o;
+  }
+  if (threadIdx.x < Hq) p.ws_ml[slot * Hq + threadIdx.x] = make_float2(sm_M[threadIdx.x], sm_L[threadIdx.x]);
+}
+
+// Log-sum-exp merge of the partition states of one sequence and a group of
+// heads: m = max_p m_p; l = sum_p l_p 2^(m_p - m); out = sum_p o_p 2^(m_p - m) / l.
+// Block = 256 threads = 8 heads x 32 float4 columns (D = 128) or 16 heads x
+// 16 columns (D = 64).
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ ws_o,
+                                                           const float2* __restrict__ ws_ml,
+                                                           float* __restrict__ out, int Hq, int P) {
+  constexpr int D4 = D / 4;
+  constexpr int HPB = 256 / D4;  // heads per block
+  const int b = blockIdx.y;
+  const int h = blockIdx.x * HPB + threadIdx.x / D4;
+  const int d0 = 4 * (threadIdx.x % D4);
+  if (h >= Hq) return;
+  const float2* ml = ws_ml + (int64_t)b * P * Hq + h;
+  const float* wo = ws_o + ((int64_t)b * P * Hq + h) * D + d0;
+  // One pass, eight partitions' loads in flight at a time, running rescale.
+  float M = -INFINITY, L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int q0 = 0; q0 < P; q0 += 8) {
+    float2 st[8];
+    f32x4 o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool live = q0 + u < P;
+      st[u] = live ? ml[(int64_t)(q0 + u) * Hq] : make_float2(-INFINITY, 0.f);
+      o[u] = live ? *reinterpret_cast<const f32x4*>(wo + (int64_t)(q0 + u) * Hq * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float Mc = M;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) Mc = fmaxf(Mc, st[u].x);
+    if (Mc == -INFINITY) continue;
+    const float a = exp2f(M - Mc);  // 0 while nothing has been seen
+    acc *= a;
+    L *= a;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = exp2f(st[u].x - Mc);  // 0 for an empty partition
+      L += st[u].y * w;
+      acc += w * o[u];
+    }
+    M = Mc;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<f32x4*>(out + ((int64_t)b * Hq + h) * D + d0) = acc * inv;
+}
+
+template <int D, int NT>
+void launch_partitions(const DecodeParams& prm, int B, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_partition_kernel<D, NT>), dim3(prm.num_parts, B), dim3(256), 0,
+                     stream, prm);
+}
+
+template <int D>
+void launch_by_heads(const DecodeParams& prm, int B, hipStream_t stream) {
+  const int nt = (prm.Hq + 15) / 16;
+  switch (nt) {
+    case 1: launch_partitions<D, 1>(prm, B, stream); break;
+    case 2: launch_partitions<D, 2>(prm, B, stream); break;
+    case 3: launch_partitions<D, 3>(prm, B, stream); break;
+    default: launch_partitions<D, 4>(prm, B, stream); break;
+  }
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+
+}  // namespace
+
+DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,
+                       int num_cus) {
+  DecodePlan pl{1, 1, 0};
+  // Upper bound of 32-key tiles a sequence's visible range can touch.
+  int64_t ntiles;
+  if (window > 0 && window < max_seq_len)
+    ntiles = (window + kTileKeys - 1) / kTileKeys + 1;  // window start may be unaligned
+  else
+    ntiles = ((int64_t)max_seq_len + kTileKeys - 1) / kTileKeys;
+  if (ntiles < 1) ntiles = 1;
+  // Aim at about two resident work-groups per compute unit, with at least one
+  // tile per wave in each work-group.
+  const int64_t target = 2 * (int64_t)(num_cus > 0 ? num_cus : 256);
+  int64_t tpp = ((int64_t)B * ntiles + target - 1) / target;
+  tpp = ((tpp + kWaves - 1) / kWaves) * kWaves;
+  if (tpp < kWaves) tpp = kWaves;
+  if (tpp > ntiles) tpp = ntiles;
+  const int64_t parts = (ntiles + tpp - 1) / tpp;
+  pl.tiles_per_part = (int)tpp;
+  pl.num_parts = (int)parts;
+  if (parts > 1) {
+    const size_t slots = (size_t)B * (size_t)parts * (size_t)Hq;
+    pl.ws_bytes = align_up(slots * sizeof(float2), 256) + align_up(slots * (size_t)D * sizeof(float), 256);
+  }
+  return pl;
+}
+
+int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const int32_t* seq_lens, int32_t B,
+                  int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
+                  void* workspace, const DecodePlan& plan, hipStream_t stream) {
+  DecodeParams prm;
+  prm.q = q;
+  prm.k = kv.k;
+  prm.v = kv.v;
+  prm.ks = kv.k_scale;
+  prm.vs = kv.v_scale;
+  prm.seq_lens = seq_lens;
+  prm.out = out;
+  prm.L_cap = kv.L_cap;
+  prm.Hq = Hq;
+  prm.window = window;
+  prm.tiles_per_part = plan.tiles_per_part;
+  prm.num_parts = plan.num_parts;
+  prm.scale_log2 = softmax_scale * 1.4426950408889634f;
+  prm.ws_o = nullptr;
+  prm.ws_ml = nullptr;
+  if (plan.num_parts > 1) {
+    const size_t slots = (size_t)B * (size_t)plan.num_parts * (size_t)Hq;
+    char* ws = static_cast<char*>(workspace);
+    prm.ws_ml = reinterpret_cast<float2*>(ws);
+    ws += align_up(slots * sizeof(float2), 256);
+    prm.ws_o = reinterpret_cast<float*>(ws);
+  }
+  if (D == 128)
+    launch_by_heads<128>(prm, B, stream);
+  else
+    launch_by_heads<64>(prm, B, stream);
+  if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
+  if (plan.num_parts > 1) {
+    const int hpb = 256 / (D / 4);
+    const dim3 grid((Hq + hpb - 1) / hpb, B);
+    if (D == 128)
+      hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(256), 0, stream, prm.ws_o, prm.ws_ml, out, Hq,
+                         plan.num_parts);
+    else
+      hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(256), 0, stream, prm.ws_o, prm.ws_ml, out, Hq,
+                         plan.num_parts);
+    if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
+  }
+  return MQA_OK;
+}
+
+}  // namespace mqa

@@ -1,0 +1,71 @@
+// kv_quantize_int8: per-token-row absmax/127 int8 encoding of new K or V rows.
+//
+// The int8 KV cache follows explinks.com "Character.AI 的最佳实践", section
+// 训练和服务的量化. The scheme (the pages leave it open): scale
+// s = fl32(absmax/127); a row whose scale is 0 is stored as zeros; otherwise
+// code = clamp(rint(fl32(x/s)), -127, 127). Both divisions are IEEE
+// correctly rounded fp32 divisions (hipcc's default for '/', denormals kept)
+// and rintf rounds half to even, so the result is bit-exact and
+// reproducible on any IEEE machine.
+//
+// Launch: one group of D/4 lanes per row; each lane owns four consecutive
+// elements (one 16-byte load, one 4-byte store), the group reduces absmax
+// with xor-shuffles. Rows are independent; this is a tiny, HBM-bound kernel.
+#include "common.h"
+#include "launch.h"
+
+namespace mqa {
+
+template <int D>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(
+    const float* __restrict__ src, int8_t* __restrict__ dst, float* __restrict__ dst_scale,
+    const int32_t* __restrict__ start_pos, int32_t B, int32_t T, int32_t L_cap) {
+  constexpr int LPR = D / 4;             // lanes per row (16 or 32)
+  constexpr int RPB = 256 / LPR;         // rows per block
+  const int lane_in_row = threadIdx.x % LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const bool live = row < (int64_t)B * T;
+  const int64_t r = live ? row : 0;
+  const int b = (int)(r / T);
+  const int t = (int)(r % T);
+
+  const float4 x = *reinterpret_cast<const float4*>(src + r * D + 4 * lane_in_row);
+  float a = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, kWave));
+
+  const float s = a / 127.0f;            // correctly rounded
+  uint32_t packed = 0;
+  if (s != 0.0f) {
+    const float v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float qv = rintf(v[i] / s);        // correctly rounded, ties to even
+      qv = fminf(fmaxf(qv, -127.0f), 127.0f);
+      packed |= ((uint32_t)(int32_t)qv & 0xffu) << (8 * i);
+    }
+  }
+  if (!live) return;
+  const int64_t pos = (int64_t)start_pos[b] + t;
+  if (pos < 0 || pos >= L_cap) return;
+  const int64_t drow = (int64_t)b * L_cap + pos;
+  *reinterpret_cast<uint32_t*>(dst + drow * D + 4 * lane_in_row) = packed;
+  if (lane_in_row == 0) dst_scale[drow] = s;
+}
+
+int launch_quantize(const float* src, int8_t* dst, float* dst_scale, const int32_t* start_pos,
+                    int32_t B, int32_t T, int32_t D, int32_t L_cap, hipStream_t stream) {
+  const int64_t rows = (int64_t)B * T;
+  const int rpb = 256 / (D / 4);
+  const int64_t grid = (rows + rpb - 1) / rpb;
+  if (grid > 0x7fffffff) return MQA_ERR_SHAPE;
+  if (D == 128)
+    hipLaunchKernelGGL(quantize_rows_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       src, dst, dst_scale, start_pos, B, T, L_cap);
+  else
+    hipLaunchKernelGGL(quantize_rows_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream,
+                       src, dst, dst_scale, start_pos, B, T, L_cap);
+  return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
+}  // namespace mqa

@@ -1,0 +1,120 @@
+"""The C-ABI library on the host (no GPU needed): exports, status strings,
+argument validation and workspace sizing. Only invalid-argument paths are
+called, which return before any HIP call; no kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mqa_int8.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mqa_attention_int8_amd as m
+    return m.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert {"kv_quantize_int8", "mqa_decode", "mqa_prefill_chunk", "mqa_decode_workspace_bytes",
+            "mqa_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in mqa_int8.h but not exported"
+
+
+def test_one_hip_runtime(lib):
+    import mqa_attention_int8_amd as m
+    assert len(m.binding.hip_runtimes_mapped()) == 1
+
+
+def test_status_strings(lib):
+    import mqa_attention_int8_amd as m
+    for code in range(7):
+        assert m.mqa_status_string(code)
+    assert m.mqa_status_string(99) == "unknown status"
+
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
+
+
+def kv(L_cap=64, k=FAKE, ks=FAKE):
+    from mqa_attention_int8_amd.binding import mqa_kv_view
+    return mqa_kv_view(k, FAKE, ks, FAKE, L_cap)
+
+
+def decode(lib, **kw):
+    a = dict(q=FAKE, kv=kv(), seq=FAKE, max_len=64, B=2, Hq=8, D=128, W=0, scale=0.1, out=FAKE,
+             ws=None, ws_bytes=0)
+    a.update(kw)
+    v = a["kv"]
+    return lib.mqa_decode(a["q"], ctypes.byref(v) if v is not None else None, a["seq"], a["max_len"], a["B"],
+                          a["Hq"], a["D"], a["W"], a["scale"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, q=None) == 1
+    assert decode(lib, kv=None) == 1
+    assert decode(lib, kv=kv(k=None)) == 1
+    assert decode(lib, B=0) == 2
+    assert decode(lib, max_len=-1) == 2
+    assert decode(lib, max_len=65) == 2                      # beyond L_cap
+    assert decode(lib, D=96) == 3
+    assert decode(lib, Hq=65) == 3
+    assert decode(lib, q=FAKE + 8) == 4
+    assert decode(lib, kv=kv(L_cap=62), max_len=60) == 4     # scales read 4 keys at a time
+    assert decode(lib, kv=kv(ks=FAKE + 4)) == 4
+    # needs a workspace (many partitions) but none given
+    assert decode(lib, kv=kv(L_cap=1 << 16), max_len=1 << 16, B=64) == 5
+
+
+def test_quantize_validation(lib):
+    assert lib.kv_quantize_int8(None, FAKE, FAKE, FAKE, 1, 1, 128, 8, None) == 1
+    assert lib.kv_quantize_int8(FAKE, FAKE, FAKE, FAKE, 1, 9, 128, 8, None) == 2
+    assert lib.kv_quantize_int8(FAKE, FAKE, FAKE, FAKE, 1, 1, 32, 8, None) == 3
+    assert lib.kv_quantize_int8(FAKE + 4, FAKE, FAKE, FAKE, 1, 1, 128, 8, None) == 4
+
+
+def test_prefill_validation(lib):
+    v = kv(L_cap=100)
+    f = lambda **k: lib.mqa_prefill_chunk(k.get("q", FAKE), ctypes.byref(v), FAKE, k.get("P", 10), 2,
+                                          k.get("C", 20), k.get("Hq", 8), k.get("D", 128), 0, 0.1,
+                                          k.get("out", FAKE), None)
+    assert f(q=None) == 1
+    assert f(C=0) == 2
+    assert f(P=81) == 2          # P + C > L_cap
+    assert f(D=80) == 3
+    assert f(out=FAKE + 2) == 4
+
+
+def test_workspace_sizes(lib):
+    import mqa_attention_int8_amd as m
+    # a single partition needs no workspace
+    assert m.mqa_decode_workspace_bytes(1, 8, 64, 128, 0) == 0
+    # many partitions: at least one fp32 accumulator + (m, l) per partition and head
+    for B, Hq, D, L, W in ((64, 32, 128, 4096, 0), (8, 32, 128, 131072, 0), (128, 32, 128, 32768, 1024)):
+        n = m.mqa_decode_workspace_bytes(B, Hq, D, L, W)
+        assert n == 0 or n >= 2 * B * Hq * (D + 2) * 4
+    assert m.mqa_decode_workspace_bytes(8, 32, 128, 131072, 0) > 0
+    assert m.mqa_decode_workspace_bytes(0, 32, 128, 4096, 0) == 0      # invalid -> 0
+
+
+def test_accounting_matches_oracle():
+    import numpy as np
+    import oracle
+    from mqa_attention_int8_amd import accounting as acct
+    import synth
+    lens = synth.HYBRID.lens()
+    for W in (0, 1024, 1):
+        assert acct.decode_kv_bytes(lens, W, 128) == oracle.decode_visible_keys(lens, W) * oracle.int8_kv_bytes_per_key(128)
+    for W in (0, 1024, 7):
+        assert acct.prefill_pairs([8192] * 3 + [5], 512, W) == oracle.prefill_visible_pairs([8192] * 3 + [5], 512, W)
+    assert acct.decode_kv_bytes(np.full(64, 4096), 0, 128) == 69_206_016
