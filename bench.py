@@ -255,6 +255,25 @@ def bench_prefill(torch, m, acct, stream):
     return res
 
 
+def counted_traffic():
+    """HBM bytes per global-layer decode call from the committed rocprofv3
+    counter summary, or None when the decode kernel source has changed since
+    the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "decode_global_traffic.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for f in rec["source_files"]:
+            h.update(open(os.path.join(root, f), "rb").read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return rec["traffic_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(budget_s: float):
     """The oracle (numpy, float64) on a bounded sample of the decode workload.
 
@@ -341,7 +360,7 @@ def main():
                    "kv_rotation_copies": dec["rotation_copies"], "graph_replay": dec["graph"]},
         "kv_read_GBps": dec["step_kv_GBps"], "kv_read_frac_hbm_peak": dec["step_kv_GBps"] / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": counted_traffic(),
                      "kernel": "mqa_decode global layer (decode_partition_kernel + decode_merge_kernel)",
                      "algorithmic_bytes_per_launch": dec["global_kv_bytes"],
                      "avg_launch_us": dec["global_call_us"]},
