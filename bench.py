@@ -239,11 +239,12 @@ def bench_prefill(torch, m, acct, stream):
     q = torch.randn((B, C, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
     plens = torch.full((B,), P, dtype=torch.int32, device="cuda")
     out = torch.empty((B, C, Hq, D), device="cuda")
+    ws = m.prefill_workspace(B, C, D, P)
     res = {"workload": "prefill_B16_C512_P8192_Hq32_D128"}
     with torch.cuda.stream(stream):
         for win in (0, 1024):
             def call():
-                m.mqa_prefill_chunk(q, kv, plens, P, win, out=out)
+                m.mqa_prefill_chunk(q, kv, plens, P, win, out=out, workspace=ws)
             call()
             torch.cuda.synchronize()
             reps = 10

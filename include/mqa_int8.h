@@ -123,6 +123,11 @@ int mqa_decode(const uint16_t* q, const mqa_kv_view* kv,
                float* out, void* workspace, size_t workspace_bytes,
                void* stream);
 
+/* Bytes of device workspace mqa_prefill_chunk needs (pure host function;
+ * 0 for invalid arguments). */
+size_t mqa_prefill_workspace_bytes(int32_t B, int32_t C, int32_t D,
+                                   int32_t max_prefix_len);
+
 /* mqa_prefill_chunk - attention of a new chunk of C tokens per sequence over
  * a cached prefix plus the chunk itself (causal).
  * [9c1h.cn page "秘訣2" (cached prefixes reused across turns); workshop
@@ -136,13 +141,17 @@ int mqa_decode(const uint16_t* q, const mqa_kv_view* kv,
  *   window       > 0: query at absolute position p sees keys
  *                max(0, p-window+1) .. p; <= 0: keys 0 .. p.
  *   out          fp32 [B, C, Hq, D].
+ *   workspace    device scratch of at least mqa_prefill_workspace_bytes()
+ *                bytes, 16-byte aligned; no initialisation needed; it holds
+ *                the chunk's key/value tiles converted once for the matrix
+ *                cores. Calls that may run concurrently must not share it.
  * Errors: NULL, SHAPE (C<=0, max_prefix_len+C > L_cap, ...), UNSUPPORTED,
- * ALIGN, HIP. */
+ * ALIGN, WORKSPACE, HIP. */
 int mqa_prefill_chunk(const uint16_t* q, const mqa_kv_view* kv,
                       const int32_t* prefix_lens, int32_t max_prefix_len,
                       int32_t B, int32_t C, int32_t Hq, int32_t D,
                       int32_t window, float softmax_scale, float* out,
-                      void* stream);
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mqa_status_string(int status);

@@ -58,8 +58,10 @@ def load_library() -> ctypes.CDLL:
         lib.mqa_decode.argtypes = [vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32, f32,
                                    vp, vp, ctypes.c_size_t, vp]
         lib.mqa_decode.restype = ctypes.c_int
+        lib.mqa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.mqa_prefill_workspace_bytes.restype = ctypes.c_size_t
         lib.mqa_prefill_chunk.argtypes = [vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32,
-                                          i32, f32, vp, vp]
+                                          i32, f32, vp, vp, ctypes.c_size_t, vp]
         lib.mqa_prefill_chunk.restype = ctypes.c_int
         _lib = lib
         return lib
@@ -187,9 +189,20 @@ def mqa_decode(q: torch.Tensor, kv: KVView, seq_lens: torch.Tensor, max_seq_len:
     return out
 
 
+def mqa_prefill_workspace_bytes(B: int, C: int, D: int, max_prefix_len: int) -> int:
+    return int(load_library().mqa_prefill_workspace_bytes(B, C, D, max_prefix_len))
+
+
+def prefill_workspace(B: int, C: int, D: int, max_prefix_len: int, device="cuda"):
+    """A workspace for mqa_prefill_chunk, reusable by any later call it fits."""
+    return torch.empty(mqa_prefill_workspace_bytes(B, C, D, max_prefix_len), dtype=torch.uint8,
+                       device=device)
+
+
 def mqa_prefill_chunk(q: torch.Tensor, kv: KVView, prefix_lens: torch.Tensor, max_prefix_len: int,
                       window: int, softmax_scale: float | None = None,
-                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                      out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
     """Causal chunk attention: q bf16 [B, C, Hq, D] -> out fp32 [B, C, Hq, D]."""
     lib = load_library()
     _need(q, torch.bfloat16, "q", 4)
@@ -198,10 +211,14 @@ def mqa_prefill_chunk(q: torch.Tensor, kv: KVView, prefix_lens: torch.Tensor, ma
     if out is None:
         out = torch.empty((B, C, Hq, D), dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out", 4)
+    if workspace is None:
+        workspace = prefill_workspace(B, C, D, max_prefix_len, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
     view = kv.c_view()
     _check(lib.mqa_prefill_chunk(_ptr(q), ctypes.byref(view), _ptr(prefix_lens), int(max_prefix_len), B,
-                                 C, Hq, D, int(window), scale, _ptr(out), _stream(stream)),
+                                 C, Hq, D, int(window), scale, _ptr(out), _ptr(workspace), ws_bytes,
+                                 _stream(stream)),
            "mqa_prefill_chunk")
     return out
 

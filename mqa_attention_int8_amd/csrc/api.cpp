@@ -65,7 +65,7 @@ const char* mqa_status_string(int status) {
     case MQA_ERR_SHAPE: return "a size argument is out of range or inconsistent";
     case MQA_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be 64 or 128, 1 <= Hq <= 64)";
     case MQA_ERR_ALIGN: return "a pointer is not suitably aligned (16 bytes for tensors, 4 for scales)";
-    case MQA_ERR_WORKSPACE: return "workspace is missing or smaller than mqa_decode_workspace_bytes()";
+    case MQA_ERR_WORKSPACE: return "workspace is missing or smaller than the size the matching *_workspace_bytes() returns";
     case MQA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     default: return "unknown status";
   }
@@ -109,18 +109,28 @@ int mqa_decode(const uint16_t* q, const mqa_kv_view* kv, const int32_t* seq_lens
                             static_cast<hipStream_t>(stream));
 }
 
+size_t mqa_prefill_workspace_bytes(int32_t B, int32_t C, int32_t D, int32_t max_prefix_len) {
+  if (B <= 0 || C <= 0 || max_prefix_len < 0 || !supported_d(D)) return 0;
+  return mqa::prefill_workspace_bytes(B, C, D, max_prefix_len);
+}
+
 int mqa_prefill_chunk(const uint16_t* q, const mqa_kv_view* kv, const int32_t* prefix_lens,
                       int32_t max_prefix_len, int32_t B, int32_t C, int32_t Hq, int32_t D,
-                      int32_t window, float softmax_scale, float* out, void* stream) {
+                      int32_t window, float softmax_scale, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   if (!q || !kv || !prefix_lens || !out) return MQA_ERR_NULL;
   if (B <= 0 || C <= 0 || Hq <= 0 || D <= 0 || max_prefix_len < 0) return MQA_ERR_SHAPE;
   if (!supported_d(D) || !supported_hq(Hq)) return MQA_ERR_UNSUPPORTED;
   int st = check_kv(kv, D);
   if (st != MQA_OK) return st;
   if ((int64_t)max_prefix_len + C > kv->L_cap) return MQA_ERR_SHAPE;
+  if ((int64_t)B > 65535) return MQA_ERR_SHAPE;  // grid.y of the staging pass
   if (!aligned16(q) || !aligned16(out)) return MQA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < mqa::prefill_workspace_bytes(B, C, D, max_prefix_len))
+    return MQA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MQA_ERR_ALIGN;
   return mqa::launch_prefill(q, *kv, prefix_lens, max_prefix_len, B, C, Hq, D, window,
-                             softmax_scale, out, static_cast<hipStream_t>(stream));
+                             softmax_scale, out, workspace, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

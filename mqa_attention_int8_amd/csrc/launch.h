@@ -25,8 +25,11 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const int32_t* seq_l
                   int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
                   void* workspace, const DecodePlan& plan, hipStream_t stream);
 
+size_t prefill_workspace_bytes(int32_t B, int32_t C, int32_t D, int32_t max_prefix_len);
+
 int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const int32_t* prefix_lens,
                    int32_t max_prefix_len, int32_t B, int32_t C, int32_t Hq, int32_t D,
-                   int32_t window, float softmax_scale, float* out, hipStream_t stream);
+                   int32_t window, float softmax_scale, float* out, void* workspace,
+                   hipStream_t stream);
 
 }  // namespace mqa

@@ -15,20 +15,26 @@
 //
 // Design for gfx950 (prefill is a dense contraction, so it runs on MFMA):
 //  * Heads are folded into rows: a sequence's chunk is a [C*Hq, D] query
-//    matrix against ONE K/V head, so every K/V tile staged in LDS serves
-//    C*Hq rows (the MQA reuse on the compute side).
-//  * Work-group = 4 waves = 128 consecutive rows; a wave owns 32 rows.
-//  * Per 64-key tile: the work-group converts the int8 K rows to bf16 into
-//    LDS ([key][d], padded rows), and the int8 V rows to bf16 TRANSPOSED
-//    ([d][key]) so that both MFMA operands are contiguous LDS reads; the
-//    per-key scales go to LDS as well (s_k pre-multiplied by scale*log2 e).
-//  * S^T = K Q^T and O^T += V^T P'^T on v_mfma_f32_16x16x32_bf16 with fp32
-//    accumulation; P' = p * s_v is split into bf16 hi + lo parts: one bf16
-//    rounding (2^-9 relative) is too coarse when a short window averages a
-//    few nearly cancelling values.
-//  * Tiles outside every row's causal/window range are skipped for the whole
-//    work-group; a wave skips tiles outside its own rows' range; only the
-//    boundary tiles apply the per-element mask.
+//    matrix against ONE K/V head, so every K/V tile serves C*Hq rows (the
+//    MQA reuse on the compute side).
+//  * Stage pass: each 64-key tile a sequence needs is converted ONCE (instead
+//    of once per work-group that reads it) into a workspace: K as bf16
+//    [key][d], V as fp16 transposed [d][key] with the keys in the order the
+//    PV product consumes them, both with 16-byte chunks XOR-swizzled so the
+//    MFMA operand reads from LDS are free of bank conflicts; plus per-key
+//    s_k * scale * log2(e), s_v and the tile's max s_v.
+//  * Attention pass: work-group = 4 waves x 32 rows; staged tiles stream
+//    global -> LDS with direct-to-LDS loads (no registers), double-buffered,
+//    the next tile in flight while the current one is computed.
+//    S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (q and K exact in bf16);
+//    O^T += V^T P'^T on v_mfma_f32_16x16x32_f16 with P' = p * s_v in fp16
+//    (2^-11 relative, inside the prefill tolerance; the int8 values are exact
+//    in fp16). To keep P' in fp16's range the softmax exponent is shifted by
+//    a per-sequence power of two E with 2^E >= max s_v, which cancels in the
+//    normalisation.
+//  * Online softmax per row (log2 domain, lazy rescale by 2^8 steps); tiles
+//    outside every row's causal/window range are skipped, boundary tiles are
+//    masked per element; work-groups of one sequence share an XCD (L2).
 #include <math.h>
 
 #include "common.h"
@@ -38,10 +44,30 @@ namespace mqa {
 
 namespace {
 
-constexpr int kKeys = 64;       // keys per LDS tile
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kKeys = 64;        // keys per tile
 constexpr int kRowsPerWave = 32;
 constexpr int kWavesP = 4;
 constexpr int kRowsPerWG = kRowsPerWave * kWavesP;
+constexpr float kLazyP = 8.0f;
+
+// Staged tile: [K bf16 64 x D][V^T fp16 D x 64][kscl 64 f32][sv 64 f32][pad]
+template <int D>
+struct StagedTile {
+  static constexpr int kBytesK = kKeys * D * 2;
+  static constexpr int kBytesV = kKeys * D * 2;
+  static constexpr int kOffScl = kBytesK + kBytesV;
+  static constexpr int kBytes = kOffScl + 1024;  // 2 x 256 B of scales + pad to 1 KB
+};
+
+__device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t cvt_pk_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
 
 struct PrefillParams {
   const uint16_t* q;
@@ -51,71 +77,180 @@ struct PrefillParams {
   const float* vs;
   const int32_t* prefix_lens;
   float* out;
+  char* stage;          // [B][ntiles][StagedTile]
+  float* tile_vmax;     // [B][ntiles]
   int32_t L_cap;
   int32_t C;
   int32_t Hq;
   int32_t window;
-  int32_t row_tiles;  // work-groups per sequence
+  int32_t ntiles;       // tiles per sequence in the workspace
+  int32_t row_tiles;    // attention work-groups per sequence
   float scale_log2;
 };
 
+__device__ __forceinline__ int clampP(int P, int L_cap, int C) {
+  return P < 0 ? 0 : (P > L_cap - C ? L_cap - C : P);
+}
+
+__device__ __forceinline__ int first_needed_key(int P, int window) {
+  return window > 0 ? max(0, P - window + 1) : 0;
+}
+
+// ---------------------------------------------------------------------------
+// Stage pass: grid (ntiles, B), 256 threads, one 64-key tile per work-group.
+// ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
-  constexpr int KSTR = D + 8;       // bf16 elements per K row in LDS
-  constexpr int VSTR = kKeys + 8;   // bf16 elements per V^T row in LDS
-  constexpr int KK = D / 32;        // MFMAs along d
-  constexpr int MT = D / 16;        // PV m-tiles (16 output columns each)
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kKeys * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VSTR];
-  __shared__ float sKs[kKeys];
-  __shared__ float sVs[kKeys];
+__global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
+  const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.L_cap, p.C);
+  const int kend = P + p.C;                            // keys [0, kend) exist
+  const int t_lo = first_needed_key(P, p.window) / kKeys;
+  const int t_hi = (kend + kKeys - 1) / kKeys;
+  if (t < t_lo || t >= t_hi) return;
+  const int base = t * kKeys;
+  char* tile = p.stage + ((int64_t)b * p.ntiles + t) * StagedTile<D>::kBytes;
+  const int8_t* kb = p.k + (int64_t)b * p.L_cap * D;
+  const int8_t* vb = p.v + (int64_t)b * p.L_cap * D;
+
+  // K: thread = (key, quarter of the row); 16-byte chunk c of row `key` is
+  // stored at chunk c ^ (key & 7).
+  {
+    constexpr int QB = D / 4;   // bytes of the row per thread (32 or 16)
+    const int key = tid >> 2, qtr = tid & 3;
+    const int j = base + key;
+    u32x4 w[QB / 16];
+#pragma unroll
+    for (int u = 0; u < QB / 16; ++u)
+      w[u] = j < kend ? *reinterpret_cast<const u32x4*>(kb + (int64_t)j * D + qtr * QB + 16 * u)
+                      : u32x4{0u, 0u, 0u, 0u};
+    uint16_t* row = reinterpret_cast<uint16_t*>(tile) + key * D;
+#pragma unroll
+    for (int u = 0; u < QB / 16; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int chunk = (qtr * QB) / 8 + 2 * u + h;   // 8 bf16 per chunk
+        const u32x4 o = cat(i8x4_to_bf16(w[u][2 * h]), i8x4_to_bf16(w[u][2 * h + 1]));
+        *reinterpret_cast<u32x4*>(row + 8 * (chunk ^ (key & 7))) = o;
+      }
+  }
+  // V^T: thread = (key group (ks, g), 4 columns). Chunk (ks, g) of row d holds
+  // the 8 keys 32ks + 16(i/4) + 4g + i%4 (i = 0..7), stored at chunk
+  // (4ks + g) ^ (d & 7) of the 64-key row.
+  {
+    constexpr int DQ = D / 4;   // 4-column groups
+    for (int it = tid; it < 8 * DQ; it += 256) {
+      const int grp = it / DQ, dq = it % DQ;
+      const int ks = grp >> 2, g = grp & 3;
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = base + 32 * ks + 16 * (i >> 2) + 4 * g + (i & 3);
+        w[i] = j < kend ? *reinterpret_cast<const uint32_t*>(vb + (int64_t)j * D + 4 * dq) : 0u;
+      }
+      uint16_t* vt = reinterpret_cast<uint16_t*>(tile + StagedTile<D>::kBytesK);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 4 * dq + e;
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) o[i >> 1] = cvt_pk_f16(i8_byte(w[i], e), i8_byte(w[i + 1], e));
+        *reinterpret_cast<u32x4*>(vt + d * kKeys + 8 * ((4 * ks + g) ^ (d & 7))) = o;
+      }
+    }
+  }
+  // Per-key scales and the tile's max s_v.
+  if (tid < kKeys) {
+    const int j = base + tid;
+    const bool ok = j < kend;
+    const float sk = ok ? p.ks[(int64_t)b * p.L_cap + j] * p.scale_log2 : 0.f;
+    const float sv = ok ? p.vs[(int64_t)b * p.L_cap + j] : 0.f;
+    float* scl = reinterpret_cast<float*>(tile + StagedTile<D>::kOffScl);
+    scl[tid] = sk;
+    scl[kKeys + tid] = sv;
+    float m = fabsf(sv);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, kWave));
+    if (tid == 0) p.tile_vmax[(int64_t)b * p.ntiles + t] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention pass.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_kernel(
+    PrefillParams p) {
+  constexpr int TB = StagedTile<D>::kBytes;
+  constexpr int KK = D / 32;        // QK MFMAs along d
+  constexpr int MT = D / 16;        // PV m-tiles
+  __shared__ __attribute__((aligned(16))) char lds[2][TB];
+  __shared__ float sm_red[kWavesP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
   const int c = lane & 15;
-  // Work-group -> (sequence, row tile). Consecutive work-groups land on
-  // different XCDs (round-robin dispatch), so map the XCD index to the
-  // sequence to keep one sequence's K/V in one L2.
+  // Work-group -> (sequence, row tile); consecutive work-groups are spread
+  // over the 8 XCDs, so give each XCD whole sequences (shared K/V in its L2).
   const int nwg = gridDim.x;
   const int lin = blockIdx.x;
   const int B = nwg / p.row_tiles;
   int b, mtile;
-  {
-    const int xcd = lin & 7;
-    const int slot = lin >> 3;
-    const int per_xcd = nwg >> 3;  // nwg is a multiple of 8 when B % 8 == 0
-    if ((B & 7) == 0) {
-      const int flat = xcd * per_xcd + slot;
-      b = flat / p.row_tiles;
-      mtile = flat % p.row_tiles;
-    } else {
-      b = lin / p.row_tiles;
-      mtile = lin % p.row_tiles;
-    }
+  if ((B & 7) == 0) {
+    const int flat = (lin & 7) * (nwg >> 3) + (lin >> 3);
+    b = flat / p.row_tiles;
+    mtile = flat % p.row_tiles;
+  } else {
+    b = lin / p.row_tiles;
+    mtile = lin % p.row_tiles;
   }
   const int C = p.C, Hq = p.Hq;
   const int rows_total = C * Hq;
-  int P = p.prefix_lens[b];
-  // keep every access inside the cache even for out-of-range lengths
-  P = P < 0 ? 0 : (P > p.L_cap - C ? p.L_cap - C : P);
+  const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.L_cap, C);
 
   const int wg_r0 = mtile * kRowsPerWG;
   const int wg_r1 = min(wg_r0 + kRowsPerWG, rows_total);
   const int w_r0 = wg_r0 + wave * kRowsPerWave;
   const int w_r1 = min(w_r0 + kRowsPerWave, rows_total);
   const bool wave_live = w_r0 < w_r1;
-
   auto key_lo = [&](int pos) { return p.window > 0 ? max(0, pos - p.window + 1) : 0; };
-  // work-group key range
   const int wg_klo = key_lo(P + wg_r0 / Hq);
   const int wg_khi = P + (wg_r1 - 1) / Hq + 1;
-  // wave key range
   const int w_klo = wave_live ? key_lo(P + w_r0 / Hq) : 0;
   const int w_khi = wave_live ? P + (w_r1 - 1) / Hq + 1 : 0;
+  const int t0 = wg_klo / kKeys;
+  const int t1 = (wg_khi + kKeys - 1) / kKeys;
+  const char* stage_b = p.stage + (int64_t)b * p.ntiles * TB;
 
-  // rows held by this lane: 16*rt + c of the wave's 32
+  // Direct-to-LDS copy of staged tile t into buffer `buf`: 1 KB per
+  // instruction per wave; the 4 waves split the tile.
+  auto issue_tile = [&](int t, int buf) {
+    const char* src = stage_b + (int64_t)t * TB;
+    for (int ch = wave; ch < TB / 1024; ch += kWavesP)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + ch * 1024 + lane * 16),
+                                       reinterpret_cast<void*>(&lds[buf][ch * 1024]), 16, 0, 0);
+  };
+  if (t0 < t1) issue_tile(t0, 0);
+
+  // Per-sequence exponent shift E (2^E >= max s_v over the staged tiles).
+  float E;
+  {
+    const int s_lo = first_needed_key(P, p.window) / kKeys;
+    const int s_hi = (P + C + kKeys - 1) / kKeys;
+    float m = 0.f;
+    for (int t = s_lo + tid; t < s_hi; t += 256) m = fmaxf(m, p.tile_vmax[(int64_t)b * p.ntiles + t]);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, kWave));
+    if (lane == 0) sm_red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
+    int e = 0;
+    if (m > 0.f) (void)frexpf(m, &e);
+    E = (float)e;
+  }
+
+  // Rows held by this lane: 16*rt + c of the wave's 32; Q^T B operand.
   int row_pos[2], row_lo[2];
   bool row_ok[2];
   bf16x8 qop[2][KK];
@@ -144,169 +279,134 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
 
-  const int8_t* kb = p.k + (int64_t)b * p.L_cap * D;
-  const int8_t* vb = p.v + (int64_t)b * p.L_cap * D;
-  const float* ksb = p.ks + (int64_t)b * p.L_cap;
-  const float* vsb = p.vs + (int64_t)b * p.L_cap;
-  const int klast = wg_khi - 1;
-
-  const int t0 = wg_klo / kKeys;
-  const int t1 = (wg_khi + kKeys - 1) / kKeys;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int t = t0; t < t1; ++t) {
+    const int buf = (t - t0) & 1;
+    if (t + 1 < t1) issue_tile(t + 1, buf ^ 1);
     const int base = t * kKeys;
-    __syncthreads();  // previous tile fully consumed
-    // ---- stage K (bf16, [key][d]) ----
-    constexpr int KSEG = D / 16;                  // 16-byte segments per row
-    for (int it = tid; it < kKeys * KSEG; it += 256) {
-      const int key = it / KSEG, seg = it % KSEG;
-      const int j = min(base + key, klast);
-      const u32x4 x = *reinterpret_cast<const u32x4*>(kb + (int64_t)j * D + 16 * seg);
-      const u32x4 a = cat(i8x4_to_bf16(x[0]), i8x4_to_bf16(x[1]));
-      const u32x4 bb = cat(i8x4_to_bf16(x[2]), i8x4_to_bf16(x[3]));
-      u32x4* dst = reinterpret_cast<u32x4*>(&sK[key * KSTR + 16 * seg]);
-      dst[0] = a;
-      dst[1] = bb;
-    }
-    // ---- stage V transposed (bf16, [d][key]) ----
-    constexpr int DQD = D / 4;                    // 4-column groups
-    for (int it = tid; it < (kKeys / 4) * DQD; it += 256) {
-      const int kq = it / DQD, dq = it % DQD;
-      uint32_t w[4];
+    const char* tl = lds[buf];
+    if (wave_live && base < w_khi && base + kKeys > w_klo) {
+      const bool need_mask = (base < w_klo) || (base + kKeys > P + w_r0 / Hq + 1) ||
+                             (p.window > 0 && base < key_lo(P + (w_r1 - 1) / Hq));
+      // ---- S^T = K Q^T ----
+      f32x4 s[4][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = min(base + 4 * kq + u, klast);
-        w[u] = *reinterpret_cast<const uint32_t*>(vb + (int64_t)j * D + 4 * dq);
-      }
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        s[kb4][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        s[kb4][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int key = 16 * kb4 + c;
+        const uint16_t* krow = reinterpret_cast<const uint16_t*>(tl) + key * D;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u32x2 o;
-        o[0] = pack_hi16(i8_byte(w[0], e), i8_byte(w[1], e));
-        o[1] = pack_hi16(i8_byte(w[2], e), i8_byte(w[3], e));
-        *reinterpret_cast<u32x2*>(&sVt[(4 * dq + e) * VSTR + 4 * kq]) = o;
-      }
-    }
-    if (tid < kKeys) {
-      const int j = base + tid;
-      const bool ok = j >= wg_klo && j < wg_khi;
-      sKs[tid] = ok ? ksb[j] * p.scale_log2 : 0.f;
-      sVs[tid] = ok ? vsb[j] : 0.f;
-    }
-    __syncthreads();
-
-    if (!wave_live || base >= w_khi || base + kKeys <= w_klo) continue;
-    const bool need_mask = (base < w_klo) || (base + kKeys > P + w_r0 / Hq + 1) ||
-                           (p.window > 0 && base < key_lo(P + (w_r1 - 1) / Hq));
-
-    // ---- S^T = K Q^T : 4 key blocks x 2 row blocks ----
-    f32x4 s[4][2];
-#pragma unroll
-    for (int kb4 = 0; kb4 < 4; ++kb4) {
-      s[kb4][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      s[kb4][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 kop =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(&sK[(16 * kb4 + c) * KSTR + 32 * kk + 8 * g]));
-        s[kb4][0] = mfma16(kop, qop[0][kk], s[kb4][0]);
-        s[kb4][1] = mfma16(kop, qop[1][kk], s[kb4][1]);
-      }
-    }
-
-    // ---- online softmax per row ----
-    bf16x8 phi[2][2], plo[2][2];  // [row block][32-key step], P' = hi + lo
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      float z[16];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = 16 * kb4 + 4 * g + r;
-          float zz = s[kb4][rt][r] * sKs[key];
-          if (need_mask) {
-            const int j = base + key;
-            zz = (j >= row_lo[rt] && j <= row_pos[rt]) ? zz : -INFINITY;
-          }
-          z[4 * kb4 + r] = zz;
-          tmax = fmaxf(tmax, zz);
+        for (int kk = 0; kk < KK; ++kk) {
+          const int chunk = (4 * kk + g) ^ (key & 7);
+          const bf16x8 kop = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * chunk));
+          s[kb4][0] = mfma16(kop, qop[0][kk], s[kb4][0]);
+          s[kb4][1] = mfma16(kop, qop[1][kk], s[kb4][1]);
         }
-      tmax = wave_max_xor(tmax, 16);
-      tmax = wave_max_xor(tmax, 32);
-      const float m_new = fmaxf(m_run[rt], tmax);
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run[rt]) != 0) {
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[rt] - m_new);
-        l_run[rt] *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) oacc[mt][rt] *= alpha;
       }
-      m_run[rt] = m_new;
-      const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+      // ---- scales of this lane's keys 16kb + 4g + r ----
+      const float* scl = reinterpret_cast<const float*>(tl + StagedTile<D>::kOffScl);
+      f32x4 kscl[4], vscl[4];
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        u32x4 wh, wl;
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        kscl[kb4] = *reinterpret_cast<const f32x4*>(scl + 16 * kb4 + 4 * g);
+        vscl[kb4] = *reinterpret_cast<const f32x4*>(scl + kKeys + 16 * kb4 + 4 * g);
+      }
+      // ---- online softmax per row ----
+      f16x8 pop[2][2];  // [row block][32-key step]
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {       // key block 2*ks2 + hh
+      for (int rt = 0; rt < 2; ++rt) {
+        float z[16];
+        float tmax = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 4; r += 2) {
-            const int zi = 4 * (2 * ks2 + hh) + r;
-            const float e0 = exp2f(z[zi] - msub);
-            const float e1 = exp2f(z[zi + 1] - msub);
-            l_run[rt] += e0 + e1;
-            const int key = 16 * (2 * ks2 + hh) + 4 * g + r;
-            const float p0 = e0 * sVs[key], p1 = e1 * sVs[key + 1];
-            const uint32_t h01 = cvt_pk_bf16(p0, p1);
-            wh[2 * hh + (r >> 1)] = h01;
-            wl[2 * hh + (r >> 1)] = cvt_pk_bf16(p0 - bf16_lo_to_f32(h01), p1 - bf16_hi_to_f32(h01));
+        for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float zz = s[kb4][rt][r] * kscl[kb4][r];
+            if (need_mask) {
+              const int j = base + 16 * kb4 + 4 * g + r;
+              zz = (j >= row_lo[rt] && j <= row_pos[rt]) ? zz : -INFINITY;
+            }
+            z[4 * kb4 + r] = zz;
+            tmax = fmaxf(tmax, zz);
           }
+        tmax = quad_max(tmax);
+        if (__builtin_amdgcn_ballot_w64(tmax > m_run[rt] + kLazyP) != 0) {
+          const float m_new = fmaxf(m_run[rt], tmax);
+          // rows of the wave may differ in position: a row with no visible key
+          // yet keeps m = -inf and must not form 2^(-inf - -inf)
+          const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[rt] - m_new);
+          m_run[rt] = m_new;
+          l_run[rt] *= alpha;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) oacc[mt][rt] *= alpha;
         }
-        phi[rt][ks2] = as_bf16x8(wh);
-        plo[rt][ks2] = as_bf16x8(wl);
+        // shift by E: p * 2^-E * s_v <= 2^8 stays in fp16 range; cancels in o / l
+        const float msub = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt] + E;
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+          u32x4 w;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const int kb4 = 2 * ks2 + hh;
+              const float e0 = fast_exp2(z[4 * kb4 + r] - msub);
+              const float e1 = fast_exp2(z[4 * kb4 + r + 1] - msub);
+              l_run[rt] += e0 + e1;
+              w[2 * hh + (r >> 1)] = cvt_pk_f16(e0 * vscl[kb4][r], e1 * vscl[kb4][r + 1]);
+            }
+          }
+          pop[rt][ks2] = __builtin_bit_cast(f16x8, w);
+        }
+      }
+      // ---- O^T += V^T P'^T (fp16) ----
+      const uint16_t* vt = reinterpret_cast<const uint16_t*>(tl + StagedTile<D>::kBytesK);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int d = 16 * mt + c;
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+          const int chunk = (4 * ks2 + g) ^ (d & 7);
+          const f16x8 vop =
+              __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(vt + d * kKeys + 8 * chunk));
+          oacc[mt][0] = mfma16_f16(vop, pop[0][ks2], oacc[mt][0]);
+          oacc[mt][1] = mfma16_f16(vop, pop[1][ks2], oacc[mt][1]);
+        }
       }
     }
-
-    // ---- O^T += V^T P'^T ----
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const uint16_t* row = &sVt[(16 * mt + c) * VSTR + 32 * ks2 + 4 * g];
-        const u32x2 lo2 = *reinterpret_cast<const u32x2*>(row);
-        const u32x2 hi2 = *reinterpret_cast<const u32x2*>(row + 16);
-        const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        const bf16x8 vop = as_bf16x8(a);
-        oacc[mt][0] = mfma16(vop, phi[0][ks2], oacc[mt][0]);
-        oacc[mt][0] = mfma16(vop, plo[0][ks2], oacc[mt][0]);
-        oacc[mt][1] = mfma16(vop, phi[1][ks2], oacc[mt][1]);
-        oacc[mt][1] = mfma16(vop, plo[1][ks2], oacc[mt][1]);
-      }
-    }
+    __builtin_amdgcn_s_waitcnt(0);   // tile t+1 has landed in LDS
+    __syncthreads();                 // ... for every wave; buffer `buf` is free
   }
 
   // ---- normalise and write: lane holds out[row 16rt + c][16mt + 4g + 0..3] ----
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    float l = l_run[rt];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    const float l = quad_sum(l_run[rt]);
     if (!row_ok[rt]) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int r = w_r0 + 16 * rt + c;
     float* dst = p.out + ((int64_t)b * rows_total + r) * D + 4 * g;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const f32x4 o = oacc[mt][rt] * inv;
-      *reinterpret_cast<f32x4*>(dst + 16 * mt) = o;
-    }
+    for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt) = oacc[mt][rt] * inv;
   }
 }
 
 }  // namespace
 
+size_t prefill_workspace_bytes(int32_t B, int32_t C, int32_t D, int32_t max_prefix_len) {
+  const int64_t ntiles = ((int64_t)max_prefix_len + C + kKeys - 1) / kKeys;
+  const size_t tb = (D == 128) ? StagedTile<128>::kBytes : StagedTile<64>::kBytes;
+  const size_t stage = (size_t)B * ntiles * tb;
+  const size_t vmax = ((size_t)B * ntiles * sizeof(float) + 255) / 256 * 256;
+  return stage + vmax;
+}
+
 int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const int32_t* prefix_lens,
                    int32_t max_prefix_len, int32_t B, int32_t C, int32_t Hq, int32_t D,
-                   int32_t window, float softmax_scale, float* out, hipStream_t stream) {
-  (void)max_prefix_len;
+                   int32_t window, float softmax_scale, float* out, void* workspace,
+                   hipStream_t stream) {
   PrefillParams prm;
   prm.q = q;
   prm.k = kv.k;
@@ -320,14 +420,22 @@ int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const int32_t* pref
   prm.Hq = Hq;
   prm.window = window;
   prm.scale_log2 = softmax_scale * 1.4426950408889634f;
+  prm.ntiles = (int)(((int64_t)max_prefix_len + C + kKeys - 1) / kKeys);
+  const size_t tb = (D == 128) ? StagedTile<128>::kBytes : StagedTile<64>::kBytes;
+  prm.stage = static_cast<char*>(workspace);
+  prm.tile_vmax = reinterpret_cast<float*>(prm.stage + (size_t)B * prm.ntiles * tb);
   const int64_t rows = (int64_t)C * Hq;
   prm.row_tiles = (int)((rows + kRowsPerWG - 1) / kRowsPerWG);
   const int64_t grid = (int64_t)prm.row_tiles * B;
   if (grid > 0x7fffffff) return MQA_ERR_SHAPE;
-  if (D == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, prm);
-  else
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, prm);
+  const dim3 sgrid(prm.ntiles, B);
+  if (D == 128) {
+    hipLaunchKernelGGL(prefill_stage_kernel<128>, sgrid, dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, prm);
+  } else {
+    hipLaunchKernelGGL(prefill_stage_kernel<64>, sgrid, dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL(prefill_attn_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, prm);
+  }
   return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 

@@ -85,14 +85,21 @@ def test_quantize_validation(lib):
 
 def test_prefill_validation(lib):
     v = kv(L_cap=100)
+    big = 1 << 30
     f = lambda **k: lib.mqa_prefill_chunk(k.get("q", FAKE), ctypes.byref(v), FAKE, k.get("P", 10), 2,
                                           k.get("C", 20), k.get("Hq", 8), k.get("D", 128), 0, 0.1,
-                                          k.get("out", FAKE), None)
+                                          k.get("out", FAKE), k.get("ws", FAKE), k.get("wsb", big), None)
     assert f(q=None) == 1
     assert f(C=0) == 2
     assert f(P=81) == 2          # P + C > L_cap
     assert f(D=80) == 3
     assert f(out=FAKE + 2) == 4
+    assert f(ws=None) == 5
+    assert f(wsb=16) == 5
+    assert f(ws=FAKE + 8) == 4
+    need = lib.mqa_prefill_workspace_bytes(2, 20, 128, 10)
+    assert need >= 2 * 64 * 128 * 2 * 2      # at least one converted K and V tile per sequence
+    assert lib.mqa_prefill_workspace_bytes(2, 0, 128, 10) == 0
 
 
 def test_workspace_sizes(lib):
