@@ -19,22 +19,25 @@
 //    MQA reuse on the compute side).
 //  * Stage pass: each 64-key tile a sequence needs is converted ONCE (instead
 //    of once per work-group that reads it) into a workspace: K as bf16
-//    [key][d], V as fp16 transposed [d][key] with the keys in the order the
-//    PV product consumes them, both with 16-byte chunks XOR-swizzled so the
-//    MFMA operand reads from LDS are free of bank conflicts; plus per-key
-//    s_k * scale * log2(e), s_v and the tile's max s_v.
+//    [key][d]; V pre-multiplied by its row scale, V'' = fp16(v * s_v * 2^-E),
+//    transposed [d][key] with the keys in the order the PV product consumes
+//    them; both with 16-byte chunks XOR-swizzled so the MFMA operand reads
+//    from LDS are free of bank conflicts; plus s_k * scale * log2(e) per key.
+//    E is a per-sequence power of two with 2^E >= max s_v (a small first
+//    pass), which keeps V'' in fp16's range; it is undone on the output.
 //  * Attention pass: work-group = 4 waves x 32 rows; staged tiles stream
 //    global -> LDS with direct-to-LDS loads (no registers), double-buffered,
 //    the next tile in flight while the current one is computed.
 //    S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (q and K exact in bf16);
-//    O^T += V^T P'^T on v_mfma_f32_16x16x32_f16 with P' = p * s_v in fp16
-//    (2^-11 relative, inside the prefill tolerance; the int8 values are exact
-//    in fp16). To keep P' in fp16's range the softmax exponent is shifted by
-//    a per-sequence power of two E with 2^E >= max s_v, which cancels in the
-//    normalisation.
-//  * Online softmax per row (log2 domain, lazy rescale by 2^8 steps); tiles
-//    outside every row's causal/window range are skipped, boundary tiles are
-//    masked per element; work-groups of one sequence share an XCD (L2).
+//    O^T += V''^T P^T on v_mfma_f32_16x16x32_f16 with P = 2^(z - m) in fp16
+//    (relative rounding 2^-11 on V'' and on P, inside the prefill
+//    tolerance), and the row sums l come from one more MFMA against an
+//    all-ones block, so they use exactly the rounded P of the product.
+//  * Softmax per element is one FMA (t = s * kscl - m_old), a max and an
+//    exp: the running max is only moved when a tile exceeds it by more than
+//    2^8 (rare path, which recomputes), so normally exp2(t) is the weight.
+//  * Tiles outside every row's causal/window range are skipped, boundary
+//    tiles are masked per element; work-groups of one sequence share an XCD.
 #include <math.h>
 
 #include "common.h"
@@ -53,13 +56,13 @@ constexpr int kWavesP = 4;
 constexpr int kRowsPerWG = kRowsPerWave * kWavesP;
 constexpr float kLazyP = 8.0f;
 
-// Staged tile: [K bf16 64 x D][V^T fp16 D x 64][kscl 64 f32][sv 64 f32][pad]
+// Staged tile: [K bf16 64 x D][V''^T fp16 D x 64][kscl 64 f32][pad to 1 KB]
 template <int D>
 struct StagedTile {
   static constexpr int kBytesK = kKeys * D * 2;
   static constexpr int kBytesV = kKeys * D * 2;
   static constexpr int kOffScl = kBytesK + kBytesV;
-  static constexpr int kBytes = kOffScl + 1024;  // 2 x 256 B of scales + pad to 1 KB
+  static constexpr int kBytes = kOffScl + 1024;  // 256 B of scales + pad to 1 KB
 };
 
 __device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
@@ -78,7 +81,7 @@ struct PrefillParams {
   const int32_t* prefix_lens;
   float* out;
   char* stage;          // [B][ntiles][StagedTile]
-  float* tile_vmax;     // [B][ntiles]
+  float* seq_e;         // [B] exponent E of each sequence (as float)
   int32_t L_cap;
   int32_t C;
   int32_t Hq;
@@ -94,6 +97,30 @@ __device__ __forceinline__ int clampP(int P, int L_cap, int C) {
 
 __device__ __forceinline__ int first_needed_key(int P, int window) {
   return window > 0 ? max(0, P - window + 1) : 0;
+}
+
+// ---------------------------------------------------------------------------
+// Exponent pass: grid (B), 256 threads. E = smallest e with 2^e >= max s_v
+// over the keys the chunk can see.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prefill_exponent_kernel(PrefillParams p) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ float red[4];
+  const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.L_cap, p.C);
+  const int lo = first_needed_key(P, p.window), hi = P + p.C;
+  const float* vs = p.vs + (int64_t)b * p.L_cap;
+  float m = 0.f;
+  for (int j = lo + tid; j < hi; j += 256) m = fmaxf(m, fabsf(vs[j]));
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, kWave));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int e = 0;
+    if (m > 0.f && m < INFINITY) (void)frexpf(m, &e);
+    p.seq_e[b] = (float)e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -133,19 +160,24 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
         *reinterpret_cast<u32x4*>(row + 8 * (chunk ^ (key & 7))) = o;
       }
   }
-  // V^T: thread = (key group (ks, g), 4 columns). Chunk (ks, g) of row d holds
-  // the 8 keys 32ks + 16(i/4) + 4g + i%4 (i = 0..7), stored at chunk
-  // (4ks + g) ^ (d & 7) of the 64-key row.
+  // V''^T: thread = (key group (ks, g), 4 columns). Chunk (ks, g) of row d
+  // holds the 8 keys 32ks + 16(i/4) + 4g + i%4 (i = 0..7), stored at chunk
+  // (4ks + g) ^ (d & 7) of the 64-key row; values fp16(v * s_v * 2^-E).
   {
     constexpr int DQ = D / 4;   // 4-column groups
+    const float rE = exp2f(-p.seq_e[b]);
+    const float* vsb = p.vs + (int64_t)b * p.L_cap;
     for (int it = tid; it < 8 * DQ; it += 256) {
       const int grp = it / DQ, dq = it % DQ;
       const int ks = grp >> 2, g = grp & 3;
       uint32_t w[8];
+      float f[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int j = base + 32 * ks + 16 * (i >> 2) + 4 * g + (i & 3);
-        w[i] = j < kend ? *reinterpret_cast<const uint32_t*>(vb + (int64_t)j * D + 4 * dq) : 0u;
+        const bool ok = j < kend;
+        w[i] = ok ? *reinterpret_cast<const uint32_t*>(vb + (int64_t)j * D + 4 * dq) : 0u;
+        f[i] = ok ? vsb[j] * rE : 0.f;   // exact: a power-of-two rescale
       }
       uint16_t* vt = reinterpret_cast<uint16_t*>(tile + StagedTile<D>::kBytesK);
 #pragma unroll
@@ -153,25 +185,124 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
         const int d = 4 * dq + e;
         u32x4 o;
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) o[i >> 1] = cvt_pk_f16(i8_byte(w[i], e), i8_byte(w[i + 1], e));
+        for (int i = 0; i < 8; i += 2)
+          o[i >> 1] = cvt_pk_f16(i8_byte(w[i], e) * f[i], i8_byte(w[i + 1], e) * f[i + 1]);
         *reinterpret_cast<u32x4*>(vt + d * kKeys + 8 * ((4 * ks + g) ^ (d & 7))) = o;
       }
     }
   }
-  // Per-key scales and the tile's max s_v.
+  // Per-key s_k * scale * log2(e).
   if (tid < kKeys) {
     const int j = base + tid;
-    const bool ok = j < kend;
-    const float sk = ok ? p.ks[(int64_t)b * p.L_cap + j] * p.scale_log2 : 0.f;
-    const float sv = ok ? p.vs[(int64_t)b * p.L_cap + j] : 0.f;
-    float* scl = reinterpret_cast<float*>(tile + StagedTile<D>::kOffScl);
-    scl[tid] = sk;
-    scl[kKeys + tid] = sv;
-    float m = fabsf(sv);
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, kWave));
-    if (tid == 0) p.tile_vmax[(int64_t)b * p.ntiles + t] = m;
+    const float sk = j < kend ? p.ks[(int64_t)b * p.L_cap + j] * p.scale_log2 : 0.f;
+    reinterpret_cast<float*>(tile + StagedTile<D>::kOffScl)[tid] = sk;
   }
+}
+
+// One 64-key tile of one wave: S^T = K Q^T, online softmax, O^T += V''^T P^T.
+// MASK: the tile straddles a row's causal or window limit.
+template <int D, bool MASK>
+__device__ __forceinline__ void prefill_tile(const char* tl, const bf16x8 (&qop)[2][D / 32],
+                                             f32x4 (&oacc)[D / 16][2], f32x4 (&lacc)[2],
+                                             float (&m_run)[2], const f16x8& ones, int base,
+                                             const int (&row_lo)[2], const int (&row_pos)[2], int g,
+                                             int c) {
+  constexpr int KK = D / 32;
+  constexpr int MT = D / 16;
+  // ---- S^T = K Q^T ----
+  f32x4 s[4][2];
+#pragma unroll
+  for (int kb4 = 0; kb4 < 4; ++kb4) {
+    s[kb4][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s[kb4][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int key = 16 * kb4 + c;
+    const uint16_t* krow = reinterpret_cast<const uint16_t*>(tl) + key * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int chunk = (4 * kk + g) ^ (key & 7);
+      const bf16x8 kop = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * chunk));
+      s[kb4][0] = mfma16(kop, qop[0][kk], s[kb4][0]);
+      s[kb4][1] = mfma16(kop, qop[1][kk], s[kb4][1]);
+    }
+  }
+  // ---- scales of this lane's keys 16kb + 4g + r ----
+  const float* scl = reinterpret_cast<const float*>(tl + StagedTile<D>::kOffScl);
+  f32x4 kscl[4];
+#pragma unroll
+  for (int kb4 = 0; kb4 < 4; ++kb4) kscl[kb4] = *reinterpret_cast<const f32x4*>(scl + 16 * kb4 + 4 * g);
+  // ---- online softmax per row: t = s * kscl - m_run, weight 2^t ----
+  f16x8 pop[2][2];  // [row block][32-key step]
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    float tz[16];
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tz[4 * kb4 + r] = fmaf(s[kb4][rt][r], kscl[kb4][r], -m_run[rt]);
+    if constexpr (MASK) {   // boundary tiles only
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = base + 16 * (i >> 2) + 4 * g + (i & 3);
+        tz[i] = (j >= row_lo[rt] && j <= row_pos[rt]) ? tz[i] : -INFINITY;
+      }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, tz[i]);
+    tmax = quad_max(tmax);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > kLazyP) != 0, 0)) {
+      // Rare: move the running max to this tile's max and rescale.
+      // (m_run = -inf makes every visible t = +inf; recompute from s.)
+      float zmax = -INFINITY;
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * kb4 + r;
+          const float z = s[kb4][rt][r] * kscl[kb4][r];
+          tz[i] = (tz[i] == -INFINITY) ? -INFINITY : z;   // keep the mask
+          zmax = fmaxf(zmax, tz[i]);
+        }
+      zmax = quad_max(zmax);
+      const float m_new = fmaxf(m_run[rt], zmax);
+      // rows of the wave may differ in position: a row with no visible key
+      // yet keeps m = -inf and must not form 2^(-inf - -inf)
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[rt] - m_new);
+      m_run[rt] = m_new;
+      lacc[rt] *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) oacc[mt][rt] *= alpha;
+      const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tz[i] -= msub;
+    }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const int zi = 8 * ks2 + i;
+        w[i >> 1] = cvt_pk_f16(fast_exp2(tz[zi]), fast_exp2(tz[zi + 1]));
+      }
+      pop[rt][ks2] = __builtin_bit_cast(f16x8, w);
+      lacc[rt] = mfma16_f16(ones, pop[rt][ks2], lacc[rt]);
+    }
+  }
+  // ---- O^T += V''^T P^T (fp16) ----
+  const uint16_t* vt = reinterpret_cast<const uint16_t*>(tl + StagedTile<D>::kBytesK);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int d = 16 * mt + c;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const int chunk = (4 * ks2 + g) ^ (d & 7);
+      const f16x8 vop =
+          __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(vt + d * kKeys + 8 * chunk));
+      oacc[mt][0] = mfma16_f16(vop, pop[0][ks2], oacc[mt][0]);
+      oacc[mt][1] = mfma16_f16(vop, pop[1][ks2], oacc[mt][1]);
+    }
+  }
+
 }
 
 // ---------------------------------------------------------------------------
@@ -184,7 +315,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int KK = D / 32;        // QK MFMAs along d
   constexpr int MT = D / 16;        // PV m-tiles
   __shared__ __attribute__((aligned(16))) char lds[2][TB];
-  __shared__ float sm_red[kWavesP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -233,22 +363,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   };
   if (t0 < t1) issue_tile(t0, 0);
 
-  // Per-sequence exponent shift E (2^E >= max s_v over the staged tiles).
-  float E;
-  {
-    const int s_lo = first_needed_key(P, p.window) / kKeys;
-    const int s_hi = (P + C + kKeys - 1) / kKeys;
-    float m = 0.f;
-    for (int t = s_lo + tid; t < s_hi; t += 256) m = fmaxf(m, p.tile_vmax[(int64_t)b * p.ntiles + t]);
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, kWave));
-    if (lane == 0) sm_red[wave] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
-    int e = 0;
-    if (m > 0.f) (void)frexpf(m, &e);
-    E = (float)e;
-  }
+  const float E = p.seq_e[b];   // output scale 2^E undoes the V'' shift
 
   // Rows held by this lane: 16*rt + c of the wave's 32; Q^T B operand.
   int row_pos[2], row_lo[2];
@@ -276,8 +391,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     oacc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     oacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};   // row sums (MFMA)
   float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+  const f16x8 ones = __builtin_bit_cast(f16x8, u32x4{0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u});
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -289,103 +405,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     if (wave_live && base < w_khi && base + kKeys > w_klo) {
       const bool need_mask = (base < w_klo) || (base + kKeys > P + w_r0 / Hq + 1) ||
                              (p.window > 0 && base < key_lo(P + (w_r1 - 1) / Hq));
-      // ---- S^T = K Q^T ----
-      f32x4 s[4][2];
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4) {
-        s[kb4][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        s[kb4][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int key = 16 * kb4 + c;
-        const uint16_t* krow = reinterpret_cast<const uint16_t*>(tl) + key * D;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const int chunk = (4 * kk + g) ^ (key & 7);
-          const bf16x8 kop = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * chunk));
-          s[kb4][0] = mfma16(kop, qop[0][kk], s[kb4][0]);
-          s[kb4][1] = mfma16(kop, qop[1][kk], s[kb4][1]);
-        }
-      }
-      // ---- scales of this lane's keys 16kb + 4g + r ----
-      const float* scl = reinterpret_cast<const float*>(tl + StagedTile<D>::kOffScl);
-      f32x4 kscl[4], vscl[4];
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4) {
-        kscl[kb4] = *reinterpret_cast<const f32x4*>(scl + 16 * kb4 + 4 * g);
-        vscl[kb4] = *reinterpret_cast<const f32x4*>(scl + kKeys + 16 * kb4 + 4 * g);
-      }
-      // ---- online softmax per row ----
-      f16x8 pop[2][2];  // [row block][32-key step]
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        float z[16];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float zz = s[kb4][rt][r] * kscl[kb4][r];
-            if (need_mask) {
-              const int j = base + 16 * kb4 + 4 * g + r;
-              zz = (j >= row_lo[rt] && j <= row_pos[rt]) ? zz : -INFINITY;
-            }
-            z[4 * kb4 + r] = zz;
-            tmax = fmaxf(tmax, zz);
-          }
-        tmax = quad_max(tmax);
-        if (__builtin_amdgcn_ballot_w64(tmax > m_run[rt] + kLazyP) != 0) {
-          const float m_new = fmaxf(m_run[rt], tmax);
-          // rows of the wave may differ in position: a row with no visible key
-          // yet keeps m = -inf and must not form 2^(-inf - -inf)
-          const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[rt] - m_new);
-          m_run[rt] = m_new;
-          l_run[rt] *= alpha;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) oacc[mt][rt] *= alpha;
-        }
-        // shift by E: p * 2^-E * s_v <= 2^8 stays in fp16 range; cancels in o / l
-        const float msub = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt] + E;
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-          u32x4 w;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-            for (int r = 0; r < 4; r += 2) {
-              const int kb4 = 2 * ks2 + hh;
-              const float e0 = fast_exp2(z[4 * kb4 + r] - msub);
-              const float e1 = fast_exp2(z[4 * kb4 + r + 1] - msub);
-              l_run[rt] += e0 + e1;
-              w[2 * hh + (r >> 1)] = cvt_pk_f16(e0 * vscl[kb4][r], e1 * vscl[kb4][r + 1]);
-            }
-          }
-          pop[rt][ks2] = __builtin_bit_cast(f16x8, w);
-        }
-      }
-      // ---- O^T += V^T P'^T (fp16) ----
-      const uint16_t* vt = reinterpret_cast<const uint16_t*>(tl + StagedTile<D>::kBytesK);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int d = 16 * mt + c;
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-          const int chunk = (4 * ks2 + g) ^ (d & 7);
-          const f16x8 vop =
-              __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(vt + d * kKeys + 8 * chunk));
-          oacc[mt][0] = mfma16_f16(vop, pop[0][ks2], oacc[mt][0]);
-          oacc[mt][1] = mfma16_f16(vop, pop[1][ks2], oacc[mt][1]);
-        }
-      }
+      if (need_mask)
+        prefill_tile<D, true>(tl, qop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g, c);
+      else
+        prefill_tile<D, false>(tl, qop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g, c);
     }
     __builtin_amdgcn_s_waitcnt(0);   // tile t+1 has landed in LDS
     __syncthreads();                 // ... for every wave; buffer `buf` is free
   }
 
   // ---- normalise and write: lane holds out[row 16rt + c][16mt + 4g + 0..3] ----
+  const float oscale = exp2f(E);
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const float l = quad_sum(l_run[rt]);
+    const float l = lacc[rt][0];   // every row of the all-ones block holds the sum
     if (!row_ok[rt]) continue;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l > 0.f ? oscale / l : 0.f;
     const int r = w_r0 + 16 * rt + c;
     float* dst = p.out + ((int64_t)b * rows_total + r) * D + 4 * g;
 #pragma unroll
@@ -399,8 +434,8 @@ size_t prefill_workspace_bytes(int32_t B, int32_t C, int32_t D, int32_t max_pref
   const int64_t ntiles = ((int64_t)max_prefix_len + C + kKeys - 1) / kKeys;
   const size_t tb = (D == 128) ? StagedTile<128>::kBytes : StagedTile<64>::kBytes;
   const size_t stage = (size_t)B * ntiles * tb;
-  const size_t vmax = ((size_t)B * ntiles * sizeof(float) + 255) / 256 * 256;
-  return stage + vmax;
+  const size_t expo = ((size_t)B * sizeof(float) + 255) / 256 * 256;
+  return stage + expo;
 }
 
 int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const int32_t* prefix_lens,
@@ -423,12 +458,13 @@ int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const int32_t* pref
   prm.ntiles = (int)(((int64_t)max_prefix_len + C + kKeys - 1) / kKeys);
   const size_t tb = (D == 128) ? StagedTile<128>::kBytes : StagedTile<64>::kBytes;
   prm.stage = static_cast<char*>(workspace);
-  prm.tile_vmax = reinterpret_cast<float*>(prm.stage + (size_t)B * prm.ntiles * tb);
+  prm.seq_e = reinterpret_cast<float*>(prm.stage + (size_t)B * prm.ntiles * tb);
   const int64_t rows = (int64_t)C * Hq;
   prm.row_tiles = (int)((rows + kRowsPerWG - 1) / kRowsPerWG);
   const int64_t grid = (int64_t)prm.row_tiles * B;
   if (grid > 0x7fffffff) return MQA_ERR_SHAPE;
   const dim3 sgrid(prm.ntiles, B);
+  hipLaunchKernelGGL(prefill_exponent_kernel, dim3(B), dim3(256), 0, stream, prm);
   if (D == 128) {
     hipLaunchKernelGGL(prefill_stage_kernel<128>, sgrid, dim3(256), 0, stream, prm);
     hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, prm);
