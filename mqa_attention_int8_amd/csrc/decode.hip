@@ -241,14 +241,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2
   constexpr int KK = D / 32;   // MFMAs along d per 16 keys
   constexpr int DPL = D / 16;  // PV m-tiles; V bytes per lane per key
   constexpr int HP = NT * 16;  // padded head count
-  constexpr int OSTR = D + 4;  // LDS row stride of the merged accumulator
+  constexpr int NK = NT * DPL; // accumulator tiles per lane
 
-  // merged accumulator, per head: column mt*16 + m holds d = DPL*m + mt
-  __shared__ __attribute__((aligned(16))) float sm_o[HP * OSTR];
+  // Raw accumulators of the 4 waves in register order: [wave][tile nt*DPL+mt][lane][r].
+  __shared__ __attribute__((aligned(16))) float sm_acc[kWaves * NK * kWave * 4];
   __shared__ float sm_m[kWaves][HP];
   __shared__ float sm_l[kWaves][HP];
-  __shared__ float sm_M[HP];
-  __shared__ float sm_L[HP];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -318,84 +316,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2
     t += kWaves;
   }
 
-  // ---- merge the 4 waves of the work-group --------------------------------
+  // ---- combine the 4 waves of the work-group --------------------------------
+  // Each wave parks its raw accumulators and (m, l) per head in LDS (lane-ordered
+  // 16-byte stores, conflict free); after one barrier, thread (w', c, r) combines
+  // the four waves' values of heads 16nt + c at dims DPL*(4w' + r) + 0..DPL-1,
+  // which are contiguous in the output row.
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    st.l_run[nt] = quad_sum(st.l_run[nt]);
+    const float l = quad_sum(st.l_run[nt]);
     if (g == 0) {
       sm_m[wave][16 * nt + c] = st.m_run[nt];
-      sm_l[wave][16 * nt + c] = st.l_run[nt];
+      sm_l[wave][16 * nt + c] = l;
     }
+#pragma unroll
+    for (int mt = 0; mt < DPL; ++mt)
+      *reinterpret_cast<f32x4*>(&sm_acc[((wave * NK + nt * DPL + mt) * kWave + lane) * 4]) = st.oacc[mt][nt];
   }
   __syncthreads();
-  if (threadIdx.x < HP) {
-    const int h = threadIdx.x;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float L = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        if (sm_m[w][h] != -INFINITY) L += sm_l[w][h] * exp2f(sm_m[w][h] - M);
-    }
-    sm_M[h] = M;
-    sm_L[h] = L;
-  }
-  __syncthreads();
+
+  const int cc = lane >> 2;  // head within a 16-head group
+  const int rr = lane & 3;   // accumulator row within the lane's 4
+  const int d0 = DPL * (4 * wave + rr);
+  const int64_t slot = (int64_t)b * p.num_parts + part;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float M = sm_M[16 * nt + c];
-    const float f = (st.m_run[nt] == -INFINITY) ? 0.f : exp2f(st.m_run[nt] - M);
+    const int h = 16 * nt + cc;
+    float mw[kWaves], f[kWaves];
+    float M = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < DPL; ++mt) st.oacc[mt][nt] *= f;
-  }
-  // Deterministic accumulation: wave 0 stores, waves 1..3 add in order.
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = sm_m[w][h];
+      M = fmaxf(M, mw[w]);
+    }
+    float L = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+    for (int w = 0; w < kWaves; ++w) {
+      f[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);  // empty wave: no weight
+      L += f[w] * sm_l[w][h];
+    }
+    float o[DPL];
 #pragma unroll
-        for (int mt = 0; mt < DPL; ++mt) {
-          f32x4* dst = reinterpret_cast<f32x4*>(&sm_o[(16 * nt + c) * OSTR + 16 * mt + 4 * g]);
-          *dst = (w == 0) ? st.oacc[mt][nt] : *dst + st.oacc[mt][nt];
-        }
+    for (int mt = 0; mt < DPL; ++mt) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        acc += f[w] * sm_acc[((w * NK + nt * DPL + mt) * kWave + 16 * wave + cc) * 4 + rr];
+      o[mt] = acc;
+    }
+    if (h < Hq) {
+      float* dst;
+      if (p.num_parts == 1) {
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+        for (int mt = 0; mt < DPL; ++mt) o[mt] *= inv;
+        dst = p.out + ((int64_t)b * Hq + h) * D + d0;
+      } else {
+        dst = p.ws_o + (slot * Hq + h) * D + d0;
+        if (wave == 0 && rr == 0) p.ws_ml[slot * Hq + h] = make_float2(M, L);
       }
-    }
-    __syncthreads();
-  }
-
-  // ---- single partition: normalise and write ---------------------------
-  constexpr int D4 = D / 4;
-  if (p.num_parts == 1) {
-    for (int e = threadIdx.x; e < Hq * D4; e += 256) {
-      const int h = e / D4, d0 = 4 * (e % D4);
-      const float L = sm_L[h];
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      f32x4 o;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int d = d0 + u;
-        o[u] = sm_o[h * OSTR + 16 * (d % DPL) + d / DPL] * inv;
-      }
-      *reinterpret_cast<f32x4*>(p.out + ((int64_t)b * Hq + h) * D + d0) = o;
+      for (int u = 0; u < DPL; u += 4)
+        *reinterpret_cast<f32x4*>(dst + u) = f32x4{o[u], o[u + 1], o[u + 2], o[u + 3]};
     }
-    return;
   }
-
-  // ---- several partitions: publish this partition's state ------------------
-  const int64_t slot = (int64_t)b * p.num_parts + part;
-  for (int e = threadIdx.x; e < Hq * D4; e += 256) {
-    const int h = e / D4, d0 = 4 * (e % D4);
-    f32x4 o;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int d = d0 + u;
-      o[u] = sm_o[h * OSTR + 16 * (d % DPL) + d / DPL];
-    }
-    *reinterpret_cast<f32x4*>(p.ws_o + (slot * Hq + h) * D + d0) = o;
-  }
-  if (threadIdx.x < Hq) p.ws_ml[slot * Hq + threadIdx.x] = make_float2(sm_M[threadIdx.x], sm_L[threadIdx.x]);
 }
 
 // Log-sum-exp merge of the partition states of one sequence and a group of
