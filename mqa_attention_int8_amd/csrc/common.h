@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mqa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -12,6 +14,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -23,7 +27,13 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_f16, same lane layout as the bf16 form.
+__device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
 
 // Pack the bf16 patterns of two fp32 values whose low 16 bits are zero (for
@@ -67,8 +77,82 @@ __device__ __forceinline__ u32x2 split_bf16(float a, float b) {
   return u32x2{h, cvt_pk_bf16(a - bf16_lo_to_f32(h), b - bf16_hi_to_f32(h))};
 }
 
+// Round-to-nearest-even fp32 -> fp16 of two values, packed (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
+// int8 -> fp16, exact, one instruction per byte: an SDWA convert sign-extends
+// the selected byte of `w` and writes the low half (upper half cleared) or the
+// high half (low half kept) of the result. hipcc does not form these itself.
+#define MQA_F16_LO(SEL)                                                                        \
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_" #SEL \
+      : "=v"(d) : "v"(w))
+#define MQA_F16_HI(SEL)                                                                             \
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_" #SEL \
+      : "+v"(d) : "v"(w))
+template <int SEL>
+__device__ __forceinline__ uint32_t f16_lo_of_byte(uint32_t w) {
+  uint32_t d;
+  if constexpr (SEL == 0) MQA_F16_LO(0);
+  else if constexpr (SEL == 1) MQA_F16_LO(1);
+  else if constexpr (SEL == 2) MQA_F16_LO(2);
+  else MQA_F16_LO(3);
+  return d;
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t f16_hi_of_byte(uint32_t d, uint32_t w) {
+  if constexpr (SEL == 0) MQA_F16_HI(0);
+  else if constexpr (SEL == 1) MQA_F16_HI(1);
+  else if constexpr (SEL == 2) MQA_F16_HI(2);
+  else MQA_F16_HI(3);
+  return d;
+}
+#undef MQA_F16_LO
+#undef MQA_F16_HI
+
+// Byte SEL of w0 and of w1 as a packed fp16 pair {w0, w1}.
+template <int SEL>
+__device__ __forceinline__ uint32_t f16_pair_of_bytes(uint32_t w0, uint32_t w1) {
+  return f16_hi_of_byte<SEL>(f16_lo_of_byte<SEL>(w0), w1);
+}
+// Four int8 codes (one word) -> four fp16 values (two words), in order.
+__device__ __forceinline__ u32x2 i8x4_to_f16(uint32_t w) {
+  return u32x2{f16_hi_of_byte<1>(f16_lo_of_byte<0>(w), w), f16_hi_of_byte<3>(f16_lo_of_byte<2>(w), w)};
+}
+
+// Split two fp32 values into fp16 hi + lo parts, both rounded to nearest
+// even: hi = fp16(x), lo = fp16(x - hi) with the difference formed exactly in
+// fp32 by a mixed-precision FMA (v_fma_mix{lo,hi}_f16). For |x| >= 2^-3 the
+// pair carries 22 significant bits; below that lo is subnormal and the
+// absolute error stays under 2^-25. Returns {hi, lo} as packed pairs.
+__device__ __forceinline__ u32x2 split_f16(float a, float b) {
+  const uint32_t hi = cvt_pk_f16(a, b);
+  uint32_t lo;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(hi), "v"(a));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(lo) : "v"(hi), "v"(b));
+  return u32x2{hi, lo};
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, I1).
+template <int I0, int I1, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < I1) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, I1>(f);
+  }
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+// Max of 8 values as a chain the compiler turns into v_max3_f32.
+__device__ __forceinline__ float max8(const float (&x)[8]) {
+  float m = fmaxf(fmaxf(x[0], x[1]), x[2]);
+  m = fmaxf(fmaxf(m, x[3]), x[4]);
+  m = fmaxf(fmaxf(m, x[5]), x[6]);
+  return fmaxf(m, x[7]);
 }
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 (v_permlane{16,32}_swap).

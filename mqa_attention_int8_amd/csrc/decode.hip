@@ -48,8 +48,16 @@ namespace mqa {
 namespace {
 
 constexpr int kTileKeys = 32;
-constexpr int kWaves = 4;
-constexpr float kLazy = 8.0f;  // rescale only when the running max grows by > 2^8
+// Waves per work-group: eight (two per SIMD) when a wave's state fits in 256
+// registers (up to 32 heads), else four. One work-group per compute unit.
+constexpr int waves_per_wg(int NT) { return NT <= 2 ? 8 : 4; }
+
+// Running offset m of the online softmax: re-based when some P'' = 2^(z - m) s_v
+// of a tile could exceed 2^kHeadroom (fp16 holds up to 65504 < 2^16), so
+// that the tile's largest P'' becomes about 2^kTarget; in between it is left
+// alone (a lazy rescale with 2^8 of slack).
+constexpr float kHeadroom = 15.0f;
+constexpr float kTarget = 7.0f;
 
 struct DecodeParams {
   const uint16_t* q;
@@ -142,15 +150,45 @@ struct WaveState {
   float l_run[NT];
 };
 
+// Rare path of the online softmax: re-base the running offset m of this head
+// group so that the tile's largest P'' = 2^(z - m) s_v is about 2^7, scaling
+// the accumulated state by 2^(m_old - m_new). Lanes whose offset is already
+// high enough keep it (alpha = 1).
+template <int D, int NT>
+__device__ __forceinline__ void rebase(WaveState<D, NT>& st, int nt, const f32x4 (&s)[2][NT],
+                                       const float (&kscl)[8], const bool (&ok)[8], bool masked, float ev,
+                                       float (&t)[8]) {
+  float z[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    z[i] = s[i >> 2][nt][i & 3] * kscl[i];
+    if (masked) z[i] = ok[i] ? z[i] : -INFINITY;
+  }
+  const float zmax = quad_max(max8(z));
+  const float m_old = st.m_run[nt];
+  const float m_new = fmaxf(m_old, zmax + (ev - kTarget));
+  const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
+  st.m_run[nt] = m_new;
+  st.l_run[nt] *= alpha;
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) st.oacc[mt][nt] *= alpha;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = (m_new == -INFINITY) ? -INFINITY : z[i] - m_new;
+}
+
+// One 32-key tile. A tile that straddles an end of the visible range [lo, hi)
+// (at most two per sequence) gives the keys outside it weight zero; the
+// branch is wave-uniform and the empty asm keeps the compiler from turning it
+// into selects executed for every tile.
 template <int D, int NT>
 __device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
-                                             const bf16x8 (&qop)[NT][D / 32],
-                                             float scale_log2, int base, int lo, int hi, int g) {
+                                             const f16x8 (&qop)[NT][D / 32],
+                                             float kscale, int base, int lo, int hi, int g) {
   constexpr int KK = D / 32;
   constexpr int DPL = D / 16;
-  const bool interior = (base >= lo) && (base + kTileKeys <= hi);
+  const bool masked = (base < lo) || (base + kTileKeys > hi);  // wave-uniform
 
-  // ---- S^T = K Q^T ---------------------------------------------------------
+  // ---- S^T = K Q'^T (fp16 operands, exact products, fp32 sums) ------------
   f32x4 s[2][NT];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
@@ -159,24 +197,24 @@ __device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const u32x4 w = cur.k[hf][kk >> 1];
-      const bf16x8 kop =
-          as_bf16x8(cat(i8x4_to_bf16(w[2 * (kk & 1)]), i8x4_to_bf16(w[2 * (kk & 1) + 1])));
+      const f16x8 kop = as_f16x8(cat(i8x4_to_f16(w[2 * (kk & 1)]), i8x4_to_f16(w[2 * (kk & 1) + 1])));
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s[hf][nt] = mfma16(kop, qop[nt][kk], s[hf][nt]);
+      for (int nt = 0; nt < NT; ++nt) s[hf][nt] = mfma16_f16(kop, qop[nt][kk], s[hf][nt]);
     }
   }
 
-  // ---- online softmax (log2 domain); P' = p * s_v as bf16 hi + lo ----------
+  // ---- online softmax (log2 domain); P'' = 2^(z - m) s_v as fp16 hi + lo ----
   float kscl[8], vscl[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    kscl[i] = cur.ks[0][i] * scale_log2;
-    kscl[4 + i] = cur.ks[1][i] * scale_log2;
+    kscl[i] = cur.ks[0][i] * kscale;
+    kscl[4 + i] = cur.ks[1][i] * kscale;
     vscl[i] = cur.vs[0][i];
     vscl[4 + i] = cur.vs[1][i];
   }
   bool ok[8];
-  if (!interior) {
+  if (masked) {
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int j = base + 16 * (i >> 2) + 4 * g + (i & 3);
@@ -184,69 +222,97 @@ __device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
       vscl[i] = ok[i] ? vscl[i] : 0.f;
     }
   }
-  bf16x8 phi[NT], plo[NT];
+  // Every s_v of the tile is below 2^ev, so every P'' is below 2^(tmax + ev).
+  const float ev = (float)__builtin_amdgcn_frexp_expf(quad_max(max8(vscl)));
+  f16x8 phi[NT], plo[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float z[8];
+    float t[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = s[i >> 2][nt][i & 3] * kscl[i];
-    if (!interior) {
+    for (int i = 0; i < 8; ++i) t[i] = fmaf(s[i >> 2][nt][i & 3], kscl[i], -st.m_run[nt]);
+    if (masked) {
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int i = 0; i < 8; ++i) z[i] = ok[i] ? z[i] : -INFINITY;
+      for (int i = 0; i < 8; ++i) t[i] = ok[i] ? t[i] : -INFINITY;
     }
-    float tmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                       fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-    tmax = quad_max(tmax);
-    if (__builtin_amdgcn_ballot_w64(tmax > st.m_run[nt] + kLazy) != 0) {
-      const float m_new = fmaxf(st.m_run[nt], tmax);
-      const float alpha = fast_exp2(st.m_run[nt] - m_new);   // 0 when m_run = -inf
-      st.m_run[nt] = m_new;
-      st.l_run[nt] *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < DPL; ++mt) st.oacc[mt][nt] *= alpha;
-    }
-    const float m_use = st.m_run[nt];
+    const float tmax = quad_max(max8(t));
+    // fp16 range guard (and the first tile, where m = -inf gives t = +inf)
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax + ev > kHeadroom) != 0, 0))
+      rebase<D, NT>(st, nt, s, kscl, ok, masked, ev, t);
     u32x4 hw, lw;
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-      const float e0 = fast_exp2(z[i] - m_use);
-      const float e1 = fast_exp2(z[i + 1] - m_use);
+      const float e0 = fast_exp2(t[i]);
+      const float e1 = fast_exp2(t[i + 1]);
       st.l_run[nt] += e0 + e1;
-      const u32x2 hl = split_bf16(e0 * vscl[i], e1 * vscl[i + 1]);
+      const u32x2 hl = split_f16(e0 * vscl[i], e1 * vscl[i + 1]);
       hw[i >> 1] = hl[0];
       lw[i >> 1] = hl[1];
     }
-    phi[nt] = as_bf16x8(hw);
-    plo[nt] = as_bf16x8(lw);
+    phi[nt] = as_f16x8(hw);
+    plo[nt] = as_f16x8(lw);
   }
 
-  // ---- O^T += V^T P'^T -------------------------------------------------------
-#pragma unroll
-  for (int mt = 0; mt < DPL; ++mt) {
+  // ---- O^T += V^T P''^T -------------------------------------------------------
+  static_for<0, DPL>([&](auto MT) {
+    constexpr int mt = decltype(MT)::value;
     u32x4 a;
 #pragma unroll
-    for (int i = 0; i < 8; i += 2)
-      a[i >> 1] = pack_hi16(i8_byte(cur.v[i][mt >> 2], mt & 3), i8_byte(cur.v[i + 1][mt >> 2], mt & 3));
-    const bf16x8 vop = as_bf16x8(a);
+    for (int i = 0; i < 8; i += 2) a[i >> 1] = f16_pair_of_bytes<mt & 3>(cur.v[i][mt >> 2], cur.v[i + 1][mt >> 2]);
+    const f16x8 vop = as_f16x8(a);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      st.oacc[mt][nt] = mfma16(vop, phi[nt], st.oacc[mt][nt]);
-      st.oacc[mt][nt] = mfma16(vop, plo[nt], st.oacc[mt][nt]);
+      st.oacc[mt][nt] = mfma16_f16(vop, phi[nt], st.oacc[mt][nt]);
+      st.oacc[mt][nt] = mfma16_f16(vop, plo[nt], st.oacc[mt][nt]);
     }
+  });
+}
+
+// The work-group's tiles pt0 + [0, count) are handed out to its waves from an
+// LDS counter, so waves that run ahead take more tiles and all finish close
+// together. Each wave keeps two tiles in registers: on entry `ta` holds the
+// loads of its tile ia and `tb` those of ib (> ia); a buffer is refilled with
+// the next handed-out tile as soon as it has been consumed.
+template <int D, int NT>
+__device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D, NT>& st, const SeqBuffers& sb,
+                                          const TileOffsets& off, const f16x8 (&qop)[NT][D / 32], float kscale,
+                                          int pt0, int count, int ia, int ib, int* next, int lane, int lo, int hi,
+                                          int g) {
+  const auto grab = [&]() {
+    int r = 0;
+    if (lane == 0) r = atomicAdd(next, 1);
+    return __builtin_amdgcn_readfirstlane(r);
+  };
+  // ia < ib at the top of the loop and handed-out indices only grow, so once
+  // ia is past the end so is ib (and vice versa in the middle).
+  while (ia < count) {
+    compute_tile<D, NT>(ta, st, qop, kscale, (pt0 + ia) * kTileKeys, lo, hi, g);
+    ia = grab();
+    load_tile<D>(ta, sb, off, (pt0 + ia) * kTileKeys, ia < count);
+    if (ib >= count) break;
+    compute_tile<D, NT>(tb, st, qop, kscale, (pt0 + ib) * kTileKeys, lo, hi, g);
+    ib = grab();
+    load_tile<D>(tb, sb, off, (pt0 + ib) * kTileKeys, ib < count);
   }
 }
 
-template <int D, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2 : 1))) void decode_partition_kernel(DecodeParams p) {
+// WINDOWED: the layer attends to the last `window` keys (the partition's
+// tiles then depend on the sequence length); otherwise to all of them.
+template <int D, int NT, bool WINDOWED>
+__global__ __launch_bounds__(64 * waves_per_wg(NT)) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2 : 1)))
+void decode_partition_kernel(DecodeParams p) {
+  constexpr int WV = waves_per_wg(NT);
+  constexpr int NTHR = 64 * WV;
   constexpr int KK = D / 32;   // MFMAs along d per 16 keys
   constexpr int DPL = D / 16;  // PV m-tiles; V bytes per lane per key
   constexpr int HP = NT * 16;  // padded head count
   constexpr int NK = NT * DPL; // accumulator tiles per lane
 
-  // Raw accumulators of the 4 waves in register order: [wave][tile nt*DPL+mt][lane][r].
-  __shared__ __attribute__((aligned(16))) float sm_acc[kWaves * NK * kWave * 4];
-  __shared__ float sm_m[kWaves][HP];
-  __shared__ float sm_l[kWaves][HP];
+  // Raw accumulators of the waves in register order: [wave][tile nt*DPL+mt][lane][r].
+  __shared__ __attribute__((aligned(16))) float sm_acc[WV * NK * kWave * 4];
+  __shared__ float sm_m[WV][HP];
+  __shared__ float sm_l[WV][HP];
+  __shared__ int sm_next;  // next tile (relative to pt0) to hand out
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -254,16 +320,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2
   const int c = lane & 15;
   const int b = blockIdx.y;
   const int part = blockIdx.x;
+  if (threadIdx.x == 0) sm_next = 2 * WV;
+  __syncthreads();
   const int Hq = p.Hq;
 
-  int n = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);  // same for the whole work-group
-  n = n < 0 ? 0 : (n > p.L_cap ? p.L_cap : n);
-  const int lo = p.window > 0 ? max(0, n - p.window) : 0;
-  const int hi = n;
-  const int t_begin = lo / kTileKeys;
-  const int t_end = hi > lo ? (hi + kTileKeys - 1) / kTileKeys : t_begin;
-  const int pt0 = t_begin + part * p.tiles_per_part;
-  const int pt1 = min(pt0 + p.tiles_per_part, t_end);
+  const int tpp = p.tiles_per_part;
 
   // One buffer resource per tensor of this sequence; loads past the cache
   // capacity return zero (rows past the valid keys are masked anyway).
@@ -277,23 +338,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2
   off.v = (uint32_t)(4 * g * D + (D / 16) * c);
   off.s = (uint32_t)(16 * g);
 
-  // First tile's loads go out before anything else.
-  Tile<D> ta, tb;
-  int t = pt0 + wave;
-  load_tile<D>(ta, sb, off, t * kTileKeys, t < pt1);
+  // Loads go out first: the q rows this lane needs and the sequence length
+  // (small, needed first); they are waited for while the memory system is
+  // still idle, since behind the tile stream they would return only once most
+  // of the chip-wide first burst of tile loads had drained. Lane (g, c) takes
+  // q[h = 16nt + c][d = g*D/4 + 8kk + 0..7] (bf16), loaded unconditionally
+  // through a buffer resource (heads past Hq read as zero).
+  u32x4 qraw[NT][KK];
+  {
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + (int64_t)b * Hq * D, (uint32_t)(Hq * D * 2));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        qraw[nt][kk] = buf_load16(qr, (uint32_t)(((16 * nt + c) * D + g * (D / 4) + 8 * kk) * 2), 0);
+  }
+  const int n_raw = p.seq_lens[b];
+  __builtin_amdgcn_s_waitcnt(0);
 
-  // Q^T as the B operand: lane holds q[h = 16nt + c][d = g*D/4 + 8kk + 0..7].
-  bf16x8 qop[NT][KK];
+  int n = __builtin_amdgcn_readfirstlane(n_raw);  // same for the whole work-group
+  n = n < 0 ? 0 : (n > p.L_cap ? p.L_cap : n);
+  const int lo = WINDOWED ? max(0, n - p.window) : 0;
+  const int hi = n;
+  const int t_begin = lo / kTileKeys;
+  const int t_end = hi > lo ? (hi + kTileKeys - 1) / kTileKeys : t_begin;
+  const int pt0 = t_begin + part * tpp;
+  const int pt1 = min(pt0 + tpp, t_end);
+  const int count = pt1 - pt0;  // tiles of this partition (may be <= 0)
+  Tile<D> ta, tb;
+  load_tile<D>(ta, sb, off, (pt0 + wave) * kTileKeys, wave < count);
+  load_tile<D>(tb, sb, off, (pt0 + wave + WV) * kTileKeys, wave + WV < count);
+
+  // Q^T as the B operand in fp16: the wave scales q by an exact power of two
+  // that puts its largest |q| in [2^14, 2^15) and folds the scale into its
+  // per-key logit factor (waves may differ; each works with true logits).
+  f16x8 qop[NT][KK];
+  float kscale;
+  {
+    float qmax = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int h = 16 * nt + c;
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (h < Hq)
-        w = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)b * Hq + h) * D + g * (D / 4) + 8 * kk);
-      qop[nt][kk] = as_bf16x8(w);
-    }
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo_to_f32(qraw[nt][kk][e])), fabsf(bf16_hi_to_f32(qraw[nt][kk][e]))));
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) qmax = wave_max_xor(qmax, m);
+    int eq = qmax > 0.f ? __builtin_amdgcn_frexp_expf(qmax) : 0;  // qmax < 2^eq
+    eq = eq < -100 ? -100 : eq;
+    const float qup = __builtin_ldexpf(1.f, 15 - eq);
+    kscale = p.scale_log2 * __builtin_ldexpf(1.f, eq - 15);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = cvt_pk_f16(bf16_lo_to_f32(qraw[nt][kk][e]) * qup, bf16_hi_to_f32(qraw[nt][kk][e]) * qup);
+        qop[nt][kk] = as_f16x8(w);
+      }
   }
 
   WaveState<D, NT> st;
@@ -305,21 +410,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2
     for (int mt = 0; mt < DPL; ++mt) st.oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Two tiles in registers, used alternately: one computing, one in flight.
-  while (t < pt1) {
-    load_tile<D>(tb, sb, off, (t + kWaves) * kTileKeys, t + kWaves < pt1);
-    compute_tile<D, NT>(ta, st, qop, p.scale_log2, t * kTileKeys, lo, hi, g);
-    t += kWaves;
-    if (t >= pt1) break;
-    load_tile<D>(ta, sb, off, (t + kWaves) * kTileKeys, t + kWaves < pt1);
-    compute_tile<D, NT>(tb, st, qop, p.scale_log2, t * kTileKeys, lo, hi, g);
-    t += kWaves;
-  }
+  run_tiles<D, NT>(ta, tb, st, sb, off, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g);
 
-  // ---- combine the 4 waves of the work-group --------------------------------
+  // ---- combine the waves of the work-group -----------------------------------
   // Each wave parks its raw accumulators and (m, l) per head in LDS (lane-ordered
-  // 16-byte stores, conflict free); after one barrier, thread (w', c, r) combines
-  // the four waves' values of heads 16nt + c at dims DPL*(4w' + r) + 0..DPL-1,
+  // 16-byte stores, conflict free); after one barrier, job (nt, g', c, r)
+  // combines all waves' values of head 16nt + c at dims DPL*(4g' + r) + 0..DPL-1,
   // which are contiguous in the output row.
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -334,23 +430,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2
   }
   __syncthreads();
 
-  const int cc = lane >> 2;  // head within a 16-head group
-  const int rr = lane & 3;   // accumulator row within the lane's 4
-  const int d0 = DPL * (4 * wave + rr);
   const int64_t slot = (int64_t)b * p.num_parts + part;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int job = threadIdx.x; job < NT * 256; job += NTHR) {
+    const int nt = job >> 8;
+    const int gq = (job >> 6) & 3;
+    const int cc = (job >> 2) & 15;
+    const int rr = job & 3;
     const int h = 16 * nt + cc;
-    float mw[kWaves], f[kWaves];
+    const int d0 = DPL * (4 * gq + rr);
+    float mw[WV], f[WV];
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < WV; ++w) {
       mw[w] = sm_m[w][h];
       M = fmaxf(M, mw[w]);
     }
     float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < WV; ++w) {
       f[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);  // empty wave: no weight
       L += f[w] * sm_l[w][h];
     }
@@ -359,8 +456,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2
     for (int mt = 0; mt < DPL; ++mt) {
       float acc = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        acc += f[w] * sm_acc[((w * NK + nt * DPL + mt) * kWave + 16 * wave + cc) * 4 + rr];
+      for (int w = 0; w < WV; ++w)
+        acc += f[w] * sm_acc[((w * NK + nt * DPL + mt) * kWave + 16 * gq + cc) * 4 + rr];
       o[mt] = acc;
     }
     if (h < Hq) {
@@ -372,7 +469,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2
         dst = p.out + ((int64_t)b * Hq + h) * D + d0;
       } else {
         dst = p.ws_o + (slot * Hq + h) * D + d0;
-        if (wave == 0 && rr == 0) p.ws_ml[slot * Hq + h] = make_float2(M, L);
+        if (gq == 0 && rr == 0) p.ws_ml[slot * Hq + h] = make_float2(M, L);
       }
 #pragma unroll
       for (int u = 0; u < DPL; u += 4)
@@ -430,8 +527,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 
 template <int D, int NT>
 void launch_partitions(const DecodeParams& prm, int B, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_partition_kernel<D, NT>), dim3(prm.num_parts, B), dim3(256), 0,
-                     stream, prm);
+  const dim3 block(64 * waves_per_wg(NT));
+  const dim3 grid(prm.num_parts, B);
+  if (prm.window > 0)
+    hipLaunchKernelGGL((decode_partition_kernel<D, NT, true>), grid, block, 0, stream, prm);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<D, NT, false>), grid, block, 0, stream, prm);
 }
 
 template <int D>
@@ -460,12 +561,11 @@ DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, in
   else
     ntiles = ((int64_t)max_seq_len + kTileKeys - 1) / kTileKeys;
   if (ntiles < 1) ntiles = 1;
-  // Aim at about two resident work-groups per compute unit, with at least one
-  // tile per wave in each work-group.
-  const int64_t target = 2 * (int64_t)(num_cus > 0 ? num_cus : 256);
+  // Aim at one work-group per compute unit, with at least one tile per wave.
+  const int64_t target = num_cus > 0 ? num_cus : 256;
+  const int64_t wv = waves_per_wg((Hq + 15) / 16);
   int64_t tpp = ((int64_t)B * ntiles + target - 1) / target;
-  tpp = ((tpp + kWaves - 1) / kWaves) * kWaves;
-  if (tpp < kWaves) tpp = kWaves;
+  if (tpp < wv) tpp = wv;
   if (tpp > ntiles) tpp = ntiles;
   const int64_t parts = (ntiles + tpp - 1) / tpp;
   pl.tiles_per_part = (int)tpp;

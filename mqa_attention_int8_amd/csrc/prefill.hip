@@ -47,9 +47,6 @@ namespace mqa {
 
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kKeys = 64;        // keys per tile
 constexpr int kRowsPerWave = 32;
 constexpr int kWavesP = 4;
@@ -64,13 +61,6 @@ struct StagedTile {
   static constexpr int kOffScl = kBytesK + kBytesV;
   static constexpr int kBytes = kOffScl + 1024;  // 256 B of scales + pad to 1 KB
 };
-
-__device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ uint32_t cvt_pk_f16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
-}
 
 struct PrefillParams {
   const uint16_t* q;
