@@ -162,6 +162,12 @@ __device__ __forceinline__ float quad_max(float v) {
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+__device__ __forceinline__ int quad_max_i(int v) {
+  const auto a = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = max((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  return max((int)b[0], (int)b[1]);
+}
 __device__ __forceinline__ float quad_sum(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);

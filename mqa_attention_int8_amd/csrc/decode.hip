@@ -52,12 +52,16 @@ constexpr int kTileKeys = 32;
 // registers (up to 32 heads), else four. One work-group per compute unit.
 constexpr int waves_per_wg(int NT) { return NT <= 2 ? 8 : 4; }
 
-// Running offset m of the online softmax: re-based when some P'' = 2^(z - m) s_v
-// of a tile could exceed 2^kHeadroom (fp16 holds up to 65504 < 2^16), so
-// that the tile's largest P'' becomes about 2^kTarget; in between it is left
-// alone (a lazy rescale with 2^8 of slack).
-constexpr float kHeadroom = 15.0f;
-constexpr float kTarget = 7.0f;
+// The PV product takes P'' = 2^(z - m) s_v 2^-vexp in fp16 (hi + lo; largest
+// finite fp16 is 65504 < 2^16), with two independent power-of-two scales:
+//  * m, the softmax offset per head, is raised lazily, only when a logit
+//    exceeds it by more than 2^kLazy (and on the first keys, m = -inf);
+//  * vexp, per wave, only rises: it is kept at (largest s_v exponent seen) - 7,
+//    so every s_v 2^-vexp < 2^7.
+// Hence P'' < 2^(kLazy + 7) = 2^15 for every key, for any scales; the
+// accumulator is rescaled when either scale moves (rare).
+constexpr float kLazy = 8.0f;
+constexpr int kValueHeadroom = 7;
 
 struct DecodeParams {
   const uint16_t* q;
@@ -67,8 +71,8 @@ struct DecodeParams {
   const float* vs;
   const int32_t* seq_lens;
   float* out;
-  float* ws_o;       // [B, P, Hq, D] partial accumulators (natural d order)
-  float2* ws_ml;     // [B, P, Hq] (max in log2 units, sum)
+  float* ws_o;       // [B, P, Hq, D] partition outputs, normalised (natural d order)
+  float2* ws_ml;     // [B, P, Hq] (offset m in log2 units, sum l of 2^(z - m))
   int32_t L_cap;
   int32_t Hq;
   int32_t window;
@@ -145,19 +149,19 @@ __device__ __forceinline__ void load_tile(Tile<D>& t, const SeqBuffers& sb, cons
 // Running state of one wave: online-softmax quantities of its NT*16 heads.
 template <int D, int NT>
 struct WaveState {
-  f32x4 oacc[D / 16][NT];
-  float m_run[NT];
-  float l_run[NT];
+  f32x4 oacc[D / 16][NT];  // sum of P'' v over the keys seen, P'' = 2^(z - m) s_v 2^-vexp
+  float m_run[NT];         // softmax offset per head (log2 units)
+  float l_run[NT];         // sum of 2^(z - m), per lane (summed over the 4 key groups at the end)
+  int vexp;                // value exponent of the wave (uniform)
 };
 
-// Rare path of the online softmax: re-base the running offset m of this head
-// group so that the tile's largest P'' = 2^(z - m) s_v is about 2^7, scaling
-// the accumulated state by 2^(m_old - m_new). Lanes whose offset is already
-// high enough keep it (alpha = 1).
+// Rare path of the online softmax for one head group: some logit of the tile
+// exceeds the offset m by more than 2^kLazy (or m = -inf). m becomes the
+// largest logit seen; the accumulated state is scaled by 2^(m_old - m_new) and
+// t is recomputed. Lanes that did not ask keep m (alpha = 1).
 template <int D, int NT>
 __device__ __forceinline__ void rebase(WaveState<D, NT>& st, int nt, const f32x4 (&s)[2][NT],
-                                       const float (&kscl)[8], const bool (&ok)[8], bool masked, float ev,
-                                       float (&t)[8]) {
+                                       const float (&kscl)[8], const bool (&ok)[8], bool masked, float (&t)[8]) {
   float z[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -166,7 +170,7 @@ __device__ __forceinline__ void rebase(WaveState<D, NT>& st, int nt, const f32x4
   }
   const float zmax = quad_max(max8(z));
   const float m_old = st.m_run[nt];
-  const float m_new = fmaxf(m_old, zmax + (ev - kTarget));
+  const float m_new = fmaxf(m_old, zmax);
   const float alpha = (m_old == -INFINITY) ? 0.f : fast_exp2(m_old - m_new);
   st.m_run[nt] = m_new;
   st.l_run[nt] *= alpha;
@@ -222,8 +226,24 @@ __device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
       vscl[i] = ok[i] ? vscl[i] : 0.f;
     }
   }
-  // Every s_v of the tile is below 2^ev, so every P'' is below 2^(tmax + ev).
-  const float ev = (float)__builtin_amdgcn_frexp_expf(quad_max(max8(vscl)));
+  // Value exponent: every s_v of the tile is below 2^(x - 126), x the largest
+  // biased exponent (s_v >= 0, so the bits compare as integers); uniform.
+  {
+    int x = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x = max(x, (int)(__float_as_uint(vscl[i]) >> 23));
+    x = __builtin_amdgcn_readfirstlane(quad_max_i(x)) - 126 - kValueHeadroom;
+    if (x > st.vexp) {  // rare: the accumulator moves to the new value scale
+      const float f = __builtin_ldexpf(1.f, max(st.vexp - x, -200));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < DPL; ++mt) st.oacc[mt][nt] *= f;
+      st.vexp = x;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vscl[i] = __builtin_ldexpf(vscl[i], -st.vexp);  // < 2^7
   f16x8 phi[NT], plo[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -236,9 +256,8 @@ __device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
       for (int i = 0; i < 8; ++i) t[i] = ok[i] ? t[i] : -INFINITY;
     }
     const float tmax = quad_max(max8(t));
-    // fp16 range guard (and the first tile, where m = -inf gives t = +inf)
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax + ev > kHeadroom) != 0, 0))
-      rebase<D, NT>(st, nt, s, kscl, ok, masked, ev, t);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > kLazy) != 0, 0))  // includes m = -inf
+      rebase<D, NT>(st, nt, s, kscl, ok, masked, t);
     u32x4 hw, lw;
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
@@ -409,6 +428,7 @@ void decode_partition_kernel(DecodeParams p) {
 #pragma unroll
     for (int mt = 0; mt < DPL; ++mt) st.oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  st.vexp = -1000;
 
   run_tiles<D, NT>(ta, tb, st, sb, off, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g);
 
@@ -417,6 +437,8 @@ void decode_partition_kernel(DecodeParams p) {
   // 16-byte stores, conflict free); after one barrier, job (nt, g', c, r)
   // combines all waves' values of head 16nt + c at dims DPL*(4g' + r) + 0..DPL-1,
   // which are contiguous in the output row.
+  // Parked states are normalised, o / l with the value scale folded back
+  // (2^vexp), so that no partial sum can overflow fp32.
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float l = quad_sum(st.l_run[nt]);
@@ -424,9 +446,14 @@ void decode_partition_kernel(DecodeParams p) {
       sm_m[wave][16 * nt + c] = st.m_run[nt];
       sm_l[wave][16 * nt + c] = l;
     }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int mt = 0; mt < DPL; ++mt)
-      *reinterpret_cast<f32x4*>(&sm_acc[((wave * NK + nt * DPL + mt) * kWave + lane) * 4]) = st.oacc[mt][nt];
+    for (int mt = 0; mt < DPL; ++mt) {
+      f32x4 o = st.oacc[mt][nt] * inv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = __builtin_ldexpf(o[r], st.vexp);
+      *reinterpret_cast<f32x4*>(&sm_acc[((wave * NK + nt * DPL + mt) * kWave + lane) * 4]) = o;
+    }
   }
   __syncthreads();
 
@@ -448,9 +475,10 @@ void decode_partition_kernel(DecodeParams p) {
     float L = 0.f;
 #pragma unroll
     for (int w = 0; w < WV; ++w) {
-      f[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);  // empty wave: no weight
-      L += f[w] * sm_l[w][h];
+      f[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M) * sm_l[w][h];  // empty wave: no weight
+      L += f[w];
     }
+    const float invL = L > 0.f ? 1.f / L : 0.f;
     float o[DPL];
 #pragma unroll
     for (int mt = 0; mt < DPL; ++mt) {
@@ -458,14 +486,11 @@ void decode_partition_kernel(DecodeParams p) {
 #pragma unroll
       for (int w = 0; w < WV; ++w)
         acc += f[w] * sm_acc[((w * NK + nt * DPL + mt) * kWave + 16 * gq + cc) * 4 + rr];
-      o[mt] = acc;
+      o[mt] = acc * invL;  // normalised: the output itself, or this partition's share
     }
     if (h < Hq) {
       float* dst;
       if (p.num_parts == 1) {
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-        for (int mt = 0; mt < DPL; ++mt) o[mt] *= inv;
         dst = p.out + ((int64_t)b * Hq + h) * D + d0;
       } else {
         dst = p.ws_o + (slot * Hq + h) * D + d0;
@@ -479,7 +504,8 @@ void decode_partition_kernel(DecodeParams p) {
 }
 
 // Log-sum-exp merge of the partition states of one sequence and a group of
-// heads: m = max_p m_p; l = sum_p l_p 2^(m_p - m); out = sum_p o_p 2^(m_p - m) / l.
+// heads, o_p normalised: m = max_p m_p; w_p = l_p 2^(m_p - m);
+// out = sum_p w_p o_p / sum_p w_p.
 // Block = 256 threads = 8 heads x 32 float4 columns (D = 128) or 16 heads x
 // 16 columns (D = 64).
 template <int D>
@@ -515,8 +541,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     L *= a;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float w = exp2f(st[u].x - Mc);  // 0 for an empty partition
-      L += st[u].y * w;
+      const float w = exp2f(st[u].x - Mc) * st[u].y;  // 0 for an empty partition
+      L += w;
       acc += w * o[u];
     }
     M = Mc;

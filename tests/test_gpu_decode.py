@@ -160,3 +160,71 @@ def test_workspace_reused_across_calls_and_shapes():
         torch.cuda.synchronize()
         ref = oracle.decode_ref(qb, *hk.arrays(), lens, W)
         assert_decode_close(out, ref, TOL, f"reuse call {it}")
+
+
+# ---- extreme scales (the fp16 P'' = 2^(z - m) s_v path and its range guard) ----------------
+#
+# Bound used below, per output element: |gpu - ref| <= 1e-5 * A + 1e-6 * Vmax, where
+# A = sum_j p_j |v_j| / l (the oracle applied to |V|) and Vmax = max visible |v_j|.
+# Each weighted term carries the fp16 hi + lo split's 2^-22 relative error (or, below 2^-3 of
+# the fp16 scale, an absolute 2^-25 against a largest P'' of at least 2^7) and fp32 sums;
+# logits stay moderate in these cases, so their fp32 rounding adds ~1e-7 relative.
+
+def scaled_rows(g, n, D, e_lo, e_hi):
+    """n rows of N(0,1) fp32 values, row r multiplied by 2^e_r with e_r uniform in [e_lo, e_hi]."""
+    x = synth.normal_f32(g, (n, D))
+    e = g.integers(e_lo, e_hi, size=n, endpoint=True)
+    return (x * np.exp2(e)[:, None]).astype(np.float32)
+
+
+def scaled_case(wid, k_exp, v_exp, q_exp=None, what="", B=4, L=1500, Hq=32, D=128, window=0):
+    lens = np.asarray([L, L - 1, 777, 33][:B], np.int32)
+    kq = np.zeros((B, L, D), np.int8); vq = np.zeros((B, L, D), np.int8)
+    ks = np.zeros((B, L), np.float32); vs = np.zeros((B, L), np.float32)
+    gk, gv = synth.rng(wid, synth.T_K, 7), synth.rng(wid, synth.T_V, 7)
+    for b in range(B):
+        kq[b], ks[b] = oracle.quantize_rows(scaled_rows(gk, L, D, *k_exp))
+        vq[b], vs[b] = oracle.quantize_rows(scaled_rows(gv, L, D, *v_exp))
+    if q_exp is None:
+        qb = q_bits(wid, (B, Hq, D))
+    else:
+        gq = synth.rng(wid, synth.T_Q, 7)
+        qf = synth.normal_f32(gq, (B, Hq, D)) * np.exp2(gq.integers(q_exp[0], q_exp[1], size=(B, Hq, D), endpoint=True))
+        qb = synth.f32_to_bf16_bits(qf.astype(np.float32))
+    hk = HostKV(kq, ks, vq, vs)
+    log(f"decode scales {what}: k 2^{k_exp} v 2^{v_exp} q {q_exp}")
+    out = run_decode(q_dev(qb), hk.to_device(), lens, int(lens.max()), window)
+    ref = oracle.decode_ref(qb, kq, ks, vq, vs, lens, window)
+    ref_abs = oracle.decode_ref(qb, kq, ks, np.abs(vq), vs, lens, window)
+    vmax = np.zeros(B)
+    for b in range(B):
+        j0 = max(0, int(lens[b]) - window) if window > 0 else 0
+        if lens[b] > j0:
+            vmax[b] = float(np.max(np.abs(vq[b, j0:lens[b]].astype(np.float64)) * vs[b, j0:lens[b], None]))
+    g = out.detach().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    bound = 1e-5 * ref_abs + 1e-6 * vmax[:, None, None]
+    excess = np.abs(g - ref) - bound
+    rel = float(np.max(np.abs(g - ref) / np.maximum(ref_abs, 1e-300)))
+    log(f"  {what}: worst |err| / A = {rel:.3e}, elements over the bound: {int((excess > 0).sum())}")
+    assert np.all(excess <= 0), f"{what}: {int((excess > 0).sum())} elements outside the bound"
+
+
+@pytest.mark.parametrize("v_exp", [(-40, 40), (90, 100), (-110, -100)])
+def test_value_scales(v_exp):
+    """Row scales of V spread over 2^80, or uniformly huge / tiny: the P'' range guard re-bases."""
+    scaled_case(80, (0, 0), v_exp, what=f"v 2^{v_exp}")
+
+
+def test_key_scales_spread():
+    """Row scales of K spread by 2^4: logits differ strongly between keys."""
+    scaled_case(81, (-2, 2), (-3, 3), what="k spread")
+
+
+def test_query_dynamic_range():
+    """q elements spread over 2^-30 .. 2^0 (the per-wave power-of-two q scaling)."""
+    scaled_case(82, (0, 0), (0, 0), q_exp=(-30, 0), what="q spread")
+
+
+def test_value_scales_window():
+    scaled_case(83, (0, 0), (-40, 40), what="v spread, window 300", window=300)
