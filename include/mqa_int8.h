@@ -123,6 +123,36 @@ int mqa_decode(const uint16_t* q, const mqa_kv_view* kv,
                float* out, void* workspace, size_t workspace_bytes,
                void* stream);
 
+/* Writable view of ONE KV buffer, for the call that appends to it. Same
+ * layout as mqa_kv_view. */
+typedef struct {
+  int8_t* k;          /* [B, L_cap, D] */
+  int8_t* v;          /* [B, L_cap, D] */
+  float* k_scale;     /* [B, L_cap] */
+  float* v_scale;     /* [B, L_cap] */
+  int32_t L_cap;
+} mqa_kv_cache;
+
+/* mqa_decode_append - one decode step of the layer that owns a KV buffer:
+ * kv_quantize_int8 of the new token's K and V rows into row seq_lens[b] - 1,
+ * then mqa_decode, in one launch. The rows written and the output are
+ * identical to those three calls. Only the first layer of a group of layers
+ * that share a buffer appends; the others call mqa_decode on the same buffer.
+ * [9c1h.cn page "秘訣1" (KV shared across layers, written once per step);
+ * explinks.com page, section 训练和服务的量化 (int8 KV).]
+ *   k_new, v_new  fp32 [B, D] (device), the new token's key and value rows.
+ *   seq_lens      keys per sequence including the new token; a sequence
+ *                 with seq_lens[b] = 0 gets no row and a zero output.
+ *   workspace     as for mqa_decode (mqa_decode_workspace_bytes of the same
+ *                 arguments).
+ * Other arguments, layout and errors as mqa_decode; k_new and v_new must be
+ * 4-byte aligned. */
+int mqa_decode_append(const uint16_t* q, const mqa_kv_cache* kv, const float* k_new,
+                      const float* v_new, const int32_t* seq_lens, int32_t max_seq_len,
+                      int32_t B, int32_t Hq, int32_t D, int32_t window,
+                      float softmax_scale, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace mqa_prefill_chunk needs (pure host function;
  * 0 for invalid arguments). */
 size_t mqa_prefill_workspace_bytes(int32_t B, int32_t C, int32_t D,

@@ -35,6 +35,11 @@ class mqa_kv_view(ctypes.Structure):
                 ("v_scale", ctypes.c_void_p), ("L_cap", ctypes.c_int32)]
 
 
+class mqa_kv_cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("L_cap", ctypes.c_int32)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -58,6 +63,9 @@ def load_library() -> ctypes.CDLL:
         lib.mqa_decode.argtypes = [vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32, f32,
                                    vp, vp, ctypes.c_size_t, vp]
         lib.mqa_decode.restype = ctypes.c_int
+        lib.mqa_decode_append.argtypes = [vp, ctypes.POINTER(mqa_kv_cache), vp, vp, vp, i32, i32, i32, i32, i32,
+                                          f32, vp, vp, ctypes.c_size_t, vp]
+        lib.mqa_decode_append.restype = ctypes.c_int
         lib.mqa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.mqa_prefill_workspace_bytes.restype = ctypes.c_size_t
         lib.mqa_prefill_chunk.argtypes = [vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32,
@@ -125,6 +133,10 @@ class KVView:
         return mqa_kv_view(self.k.data_ptr(), self.v.data_ptr(), self.k_scale.data_ptr(),
                            self.v_scale.data_ptr(), self.L_cap)
 
+    def c_cache(self) -> mqa_kv_cache:
+        return mqa_kv_cache(self.k.data_ptr(), self.v.data_ptr(), self.k_scale.data_ptr(),
+                            self.v_scale.data_ptr(), self.L_cap)
+
 
 def kv_quantize_int8(src: torch.Tensor, dst: torch.Tensor, dst_scale: torch.Tensor,
                      start_pos: torch.Tensor, stream=None) -> None:
@@ -186,6 +198,36 @@ def mqa_decode(q: torch.Tensor, kv: KVView, seq_lens: torch.Tensor, max_seq_len:
     _check(lib.mqa_decode(_ptr(q), ctypes.byref(view), _ptr(seq_lens), int(max_seq_len), B, Hq, D,
                           int(window), scale, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
            "mqa_decode")
+    return out
+
+
+def mqa_decode_append(q: torch.Tensor, kv: KVView, k_new: torch.Tensor, v_new: torch.Tensor,
+                      seq_lens: torch.Tensor, max_seq_len: int, window: int,
+                      softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Append the new token's K/V rows (fp32 [B, D]) at row seq_lens[b] - 1 of
+    ``kv`` and run one decode step on it, in one launch."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q", 3)
+    _need(seq_lens, torch.int32, "seq_lens", 1)
+    B, Hq, D = (int(x) for x in q.shape)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, torch.float32, n, 2)
+        if tuple(t.shape) != (B, D):
+            raise ValueError(f"{n} must have shape {(B, D)}")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out", 3)
+    need = mqa_decode_workspace_bytes(B, Hq, D, max_seq_len, window)
+    if workspace is None and need > 0:
+        workspace = decode_workspace(B, Hq, D, max_seq_len, window, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
+    cache = kv.c_cache()
+    _check(lib.mqa_decode_append(_ptr(q), ctypes.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
+                                 int(max_seq_len), B, Hq, D, int(window), scale, _ptr(out), _ptr(workspace),
+                                 ws_bytes, _stream(stream)),
+           "mqa_decode_append")
     return out
 
 

@@ -109,6 +109,31 @@ int mqa_decode(const uint16_t* q, const mqa_kv_view* kv, const int32_t* seq_lens
                             static_cast<hipStream_t>(stream));
 }
 
+int mqa_decode_append(const uint16_t* q, const mqa_kv_cache* kv, const float* k_new, const float* v_new,
+                      const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq, int32_t D,
+                      int32_t window, float softmax_scale, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!kv || !k_new || !v_new) return MQA_ERR_NULL;
+  if (((uintptr_t)k_new & 3u) || ((uintptr_t)v_new & 3u)) return MQA_ERR_ALIGN;
+  const mqa_kv_view view{kv->k, kv->v, kv->k_scale, kv->v_scale, kv->L_cap};
+  if (!q || !seq_lens || !out) return MQA_ERR_NULL;
+  int st = check_decode_shape(B, Hq, D, max_seq_len);
+  if (st != MQA_OK) return st;
+  st = check_kv(&view, D);
+  if (st != MQA_OK) return st;
+  if (max_seq_len > kv->L_cap) return MQA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(out)) return MQA_ERR_ALIGN;
+  if ((kv->L_cap & 3) || !aligned16(kv->k_scale) || !aligned16(kv->v_scale)) return MQA_ERR_ALIGN;
+  const mqa::DecodePlan plan = mqa::plan_decode(B, Hq, D, max_seq_len, window, device_cu_count());
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+  }
+  const mqa::AppendRows rows{k_new, v_new, kv->k, kv->v, kv->k_scale, kv->v_scale};
+  return mqa::launch_decode(q, view, seq_lens, B, Hq, D, window, softmax_scale, out, workspace, plan,
+                            static_cast<hipStream_t>(stream), &rows);
+}
+
 size_t mqa_prefill_workspace_bytes(int32_t B, int32_t C, int32_t D, int32_t max_prefix_len) {
   if (B <= 0 || C <= 0 || max_prefix_len < 0 || !supported_d(D)) return 0;
   return mqa::prefill_workspace_bytes(B, C, D, max_prefix_len);

@@ -134,6 +134,18 @@ __device__ __forceinline__ u32x2 split_f16(float a, float b) {
   return u32x2{hi, lo};
 }
 
+// int8 KV encoding of one value (the library's quantizer and the fused append
+// share these, so both write identical bytes): scale s = fl32(absmax / 127),
+// code = clamp(rint(fl32(x / s)), -127, 127); both divisions are IEEE
+// correctly rounded fp32 divisions and rintf rounds half to even. A row whose
+// scale is 0 is all zero codes.
+__device__ __forceinline__ float kv_row_scale(float absmax) { return absmax / 127.0f; }
+__device__ __forceinline__ int kv_code(float x, float s) {
+  if (s == 0.0f) return 0;
+  const float qv = rintf(x / s);
+  return (int)fminf(fmaxf(qv, -127.0f), 127.0f);
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, I1).
 template <int I0, int I1, typename F>
 __device__ __forceinline__ void static_for(F&& f) {

@@ -48,9 +48,12 @@ namespace mqa {
 namespace {
 
 constexpr int kTileKeys = 32;
-// Waves per work-group: eight (two per SIMD) when a wave's state fits in 256
-// registers (up to 32 heads), else four. One work-group per compute unit.
-constexpr int waves_per_wg(int NT) { return NT <= 2 ? 8 : 4; }
+// Waves per work-group: eight, two per SIMD (a wave's state for up to 32
+// heads fits in 256 registers). One work-group per compute unit.
+constexpr int kWavesPerWG = 8;
+// Heads per work-group: a layer with more query heads is split into groups of
+// 32 (grid z), each of which reads the key/value tiles itself.
+constexpr int kHeadsPerGroup = 32;
 
 // The PV product takes P'' = 2^(z - m) s_v 2^-vexp in fp16 (hi + lo; largest
 // finite fp16 is 65504 < 2^16), with two independent power-of-two scales:
@@ -71,6 +74,14 @@ struct DecodeParams {
   const float* vs;
   const int32_t* seq_lens;
   float* out;
+  // Fused append (k_new != nullptr): the new token's K and V rows, fp32 [B, D],
+  // are encoded into row seq_lens[b] - 1 of the (writable) cache.
+  const float* k_new;
+  const float* v_new;
+  int8_t* k_w;
+  int8_t* v_w;
+  float* ks_w;
+  float* vs_w;
   float* ws_o;       // [B, P, Hq, D] partition outputs, normalised (natural d order)
   float2* ws_ml;     // [B, P, Hq] (offset m in log2 units, sum l of 2^(z - m))
   int32_t L_cap;
@@ -287,16 +298,51 @@ __device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
   });
 }
 
+// Fused append: the tile holding the new key (row r of the tile) was loaded
+// from the cache, possibly before the row was written; its bytes and scales
+// are replaced in registers by the encoded row kept in LDS (K codes at nk[0,D),
+// V codes at nk[D, 2D), scales at ns[0..1]). Selects only: no divergence.
+template <int D>
+__device__ __forceinline__ void patch_new_row(Tile<D>& t, const int8_t* nk, const float* ns, int r, int g, int c) {
+  const int hfr = r >> 4, cr = r & 15, gr = cr >> 2, ir = cr & 3;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int w = 0; w < Tile<D>::KV4; ++w) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(nk + g * (D / 4) + 16 * w);
+      if (hf == hfr && c == cr) t.k[hf][w] = v;
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int w = 0; w < Tile<D>::VW; ++w) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(nk + D + c * (D / 16) + 4 * w);
+      if (i == 4 * hfr + ir && g == gr) t.v[i][w] = v;
+    }
+  const float sk = ns[0], sv = ns[1];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (hf == hfr && e == ir && g == gr) {
+        t.ks[hf][e] = sk;
+        t.vs[hf][e] = sv;
+      }
+}
+
 // The work-group's tiles pt0 + [0, count) are handed out to its waves from an
-// LDS counter, so waves that run ahead take more tiles and all finish close
-// together. Each wave keeps two tiles in registers: on entry `ta` holds the
-// loads of its tile ia and `tb` those of ib (> ia); a buffer is refilled with
-// the next handed-out tile as soon as it has been consumed.
+// LDS counter, so waves that run ahead (the SIMDs favour older waves) take
+// more tiles and all finish close together. Which wave sums which tile then
+// depends on timing, so results can differ between runs in the last bits.
+// Each wave keeps two tiles in registers: on entry `ta` holds the loads of its
+// tile ia and `tb` those of ib (> ia); a buffer is refilled with the next
+// handed-out tile as soon as it has been consumed.
 template <int D, int NT>
 __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D, NT>& st, const SeqBuffers& sb,
                                           const TileOffsets& off, const f16x8 (&qop)[NT][D / 32], float kscale,
                                           int pt0, int count, int ia, int ib, int* next, int lane, int lo, int hi,
-                                          int g) {
+                                          int g, int new_tile, const int8_t* nk, const float* ns) {
+  const int c = lane & 15;
   const auto grab = [&]() {
     int r = 0;
     if (lane == 0) r = atomicAdd(next, 1);
@@ -305,10 +351,12 @@ __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D,
   // ia < ib at the top of the loop and handed-out indices only grow, so once
   // ia is past the end so is ib (and vice versa in the middle).
   while (ia < count) {
+    if (ia == new_tile) patch_new_row<D>(ta, nk, ns, hi - 1 - (pt0 + ia) * kTileKeys, g, c);
     compute_tile<D, NT>(ta, st, qop, kscale, (pt0 + ia) * kTileKeys, lo, hi, g);
     ia = grab();
     load_tile<D>(ta, sb, off, (pt0 + ia) * kTileKeys, ia < count);
     if (ib >= count) break;
+    if (ib == new_tile) patch_new_row<D>(tb, nk, ns, hi - 1 - (pt0 + ib) * kTileKeys, g, c);
     compute_tile<D, NT>(tb, st, qop, kscale, (pt0 + ib) * kTileKeys, lo, hi, g);
     ib = grab();
     load_tile<D>(tb, sb, off, (pt0 + ib) * kTileKeys, ib < count);
@@ -318,9 +366,10 @@ __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D,
 // WINDOWED: the layer attends to the last `window` keys (the partition's
 // tiles then depend on the sequence length); otherwise to all of them.
 template <int D, int NT, bool WINDOWED>
-__global__ __launch_bounds__(64 * waves_per_wg(NT)) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 2 : 1)))
+__global__ __launch_bounds__(64 * kWavesPerWG) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partition_kernel(DecodeParams p) {
-  constexpr int WV = waves_per_wg(NT);
+  static_assert(NT == 1 || NT == 2, "a work-group serves at most 32 heads");
+  constexpr int WV = kWavesPerWG;
   constexpr int NTHR = 64 * WV;
   constexpr int KK = D / 32;   // MFMAs along d per 16 keys
   constexpr int DPL = D / 16;  // PV m-tiles; V bytes per lane per key
@@ -332,6 +381,9 @@ void decode_partition_kernel(DecodeParams p) {
   __shared__ float sm_m[WV][HP];
   __shared__ float sm_l[WV][HP];
   __shared__ int sm_next;  // next tile (relative to pt0) to hand out
+  __shared__ __attribute__((aligned(16))) int8_t sm_new[2 * D];  // fused append: encoded K, V row
+  __shared__ float sm_news[2];                                   // ... and its two scales
+  __shared__ float sm_amax[WV];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -341,7 +393,9 @@ void decode_partition_kernel(DecodeParams p) {
   const int part = blockIdx.x;
   if (threadIdx.x == 0) sm_next = 2 * WV;
   __syncthreads();
-  const int Hq = p.Hq;
+  const int Hq = p.Hq;                     // heads of the layer (row stride of q and out)
+  const int h0 = kHeadsPerGroup * (int)blockIdx.z;   // first head of this group
+  const int Hg = min(Hq - h0, NT * 16);    // heads of this group
 
   const int tpp = p.tiles_per_part;
 
@@ -365,7 +419,7 @@ void decode_partition_kernel(DecodeParams p) {
   // through a buffer resource (heads past Hq read as zero).
   u32x4 qraw[NT][KK];
   {
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + (int64_t)b * Hq * D, (uint32_t)(Hq * D * 2));
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + ((int64_t)b * Hq + h0) * D, (uint32_t)(Hg * D * 2));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -373,6 +427,11 @@ void decode_partition_kernel(DecodeParams p) {
         qraw[nt][kk] = buf_load16(qr, (uint32_t)(((16 * nt + c) * D + g * (D / 4) + 8 * kk) * 2), 0);
   }
   const int n_raw = p.seq_lens[b];
+  // fused append: thread x < D holds k_new[b][x], D <= x < 2D holds v_new[b][x - D]
+  const bool appending = p.k_new != nullptr;
+  float xnew = 0.f;
+  if (appending && threadIdx.x < 2 * D)
+    xnew = threadIdx.x < D ? p.k_new[(int64_t)b * D + threadIdx.x] : p.v_new[(int64_t)b * D + threadIdx.x - D];
   __builtin_amdgcn_s_waitcnt(0);
 
   int n = __builtin_amdgcn_readfirstlane(n_raw);  // same for the whole work-group
@@ -384,6 +443,39 @@ void decode_partition_kernel(DecodeParams p) {
   const int pt0 = t_begin + part * tpp;
   const int pt1 = min(pt0 + tpp, t_end);
   const int count = pt1 - pt0;  // tiles of this partition (may be <= 0)
+  // Fused append: the work-group whose range holds row n - 1 encodes the new
+  // row (the same arithmetic as kv_quantize_int8), writes it to the cache and
+  // keeps it in LDS for the wave that computes that tile.
+  int new_tile = -1;
+  if (appending && n > 0 && (n - 1) / kTileKeys >= pt0 && (n - 1) / kTileKeys < pt1) {
+    new_tile = (n - 1) / kTileKeys - pt0;
+    float a = fabsf(xnew);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, kWave));
+    if (lane == 0) sm_amax[wave] = a;
+    __syncthreads();
+    const int tw = (int)threadIdx.x < D ? 0 : 1;  // tensor of this thread: K or V
+    float amax = 0.f;
+    for (int w = tw * (D / 64); w < (tw + 1) * (D / 64); ++w) amax = fmaxf(amax, sm_amax[w]);
+    const float sc = kv_row_scale(amax);
+    if (threadIdx.x < 2 * D) {
+      const int8_t code = (int8_t)kv_code(xnew, sc);
+      sm_new[threadIdx.x] = code;
+      const int64_t row = (int64_t)b * p.L_cap + (n - 1);
+      if (blockIdx.z != 0) {
+        // another head group writes the row; this one only needs it in LDS
+        if (threadIdx.x == 0) sm_news[0] = sc;
+        if (threadIdx.x == D) sm_news[1] = sc;
+      } else if (tw == 0) {
+        p.k_w[row * D + threadIdx.x] = code;
+        if (threadIdx.x == 0) { p.ks_w[row] = sc; sm_news[0] = sc; }
+      } else {
+        p.v_w[row * D + threadIdx.x - D] = code;
+        if (threadIdx.x == D) { p.vs_w[row] = sc; sm_news[1] = sc; }
+      }
+    }
+    __syncthreads();
+  }
   Tile<D> ta, tb;
   load_tile<D>(ta, sb, off, (pt0 + wave) * kTileKeys, wave < count);
   load_tile<D>(tb, sb, off, (pt0 + wave + WV) * kTileKeys, wave + WV < count);
@@ -430,7 +522,8 @@ void decode_partition_kernel(DecodeParams p) {
   }
   st.vexp = -1000;
 
-  run_tiles<D, NT>(ta, tb, st, sb, off, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g);
+  run_tiles<D, NT>(ta, tb, st, sb, off, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g,
+                   new_tile, sm_new, sm_news);
 
   // ---- combine the waves of the work-group -----------------------------------
   // Each wave parks its raw accumulators and (m, l) per head in LDS (lane-ordered
@@ -488,13 +581,13 @@ void decode_partition_kernel(DecodeParams p) {
         acc += f[w] * sm_acc[((w * NK + nt * DPL + mt) * kWave + 16 * gq + cc) * 4 + rr];
       o[mt] = acc * invL;  // normalised: the output itself, or this partition's share
     }
-    if (h < Hq) {
+    if (h < Hg) {
       float* dst;
       if (p.num_parts == 1) {
-        dst = p.out + ((int64_t)b * Hq + h) * D + d0;
+        dst = p.out + ((int64_t)b * Hq + h0 + h) * D + d0;
       } else {
-        dst = p.ws_o + (slot * Hq + h) * D + d0;
-        if (gq == 0 && rr == 0) p.ws_ml[slot * Hq + h] = make_float2(M, L);
+        dst = p.ws_o + (slot * Hq + h0 + h) * D + d0;
+        if (gq == 0 && rr == 0) p.ws_ml[slot * Hq + h0 + h] = make_float2(M, L);
       }
 #pragma unroll
       for (int u = 0; u < DPL; u += 4)
@@ -553,8 +646,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 
 template <int D, int NT>
 void launch_partitions(const DecodeParams& prm, int B, hipStream_t stream) {
-  const dim3 block(64 * waves_per_wg(NT));
-  const dim3 grid(prm.num_parts, B);
+  const dim3 block(64 * kWavesPerWG);
+  const dim3 grid(prm.num_parts, B, (prm.Hq + kHeadsPerGroup - 1) / kHeadsPerGroup);
   if (prm.window > 0)
     hipLaunchKernelGGL((decode_partition_kernel<D, NT, true>), grid, block, 0, stream, prm);
   else
@@ -563,13 +656,10 @@ void launch_partitions(const DecodeParams& prm, int B, hipStream_t stream) {
 
 template <int D>
 void launch_by_heads(const DecodeParams& prm, int B, hipStream_t stream) {
-  const int nt = (prm.Hq + 15) / 16;
-  switch (nt) {
-    case 1: launch_partitions<D, 1>(prm, B, stream); break;
-    case 2: launch_partitions<D, 2>(prm, B, stream); break;
-    case 3: launch_partitions<D, 3>(prm, B, stream); break;
-    default: launch_partitions<D, 4>(prm, B, stream); break;
-  }
+  if (prm.Hq <= 16)
+    launch_partitions<D, 1>(prm, B, stream);
+  else
+    launch_partitions<D, 2>(prm, B, stream);
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -589,8 +679,9 @@ DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, in
   if (ntiles < 1) ntiles = 1;
   // Aim at one work-group per compute unit, with at least one tile per wave.
   const int64_t target = num_cus > 0 ? num_cus : 256;
-  const int64_t wv = waves_per_wg((Hq + 15) / 16);
-  int64_t tpp = ((int64_t)B * ntiles + target - 1) / target;
+  const int64_t wv = kWavesPerWG;
+  const int64_t groups = (Hq + kHeadsPerGroup - 1) / kHeadsPerGroup;
+  int64_t tpp = ((int64_t)B * groups * ntiles + target - 1) / target;
   if (tpp < wv) tpp = wv;
   if (tpp > ntiles) tpp = ntiles;
   const int64_t parts = (ntiles + tpp - 1) / tpp;
@@ -605,8 +696,14 @@ DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, in
 
 int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const int32_t* seq_lens, int32_t B,
                   int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
-                  void* workspace, const DecodePlan& plan, hipStream_t stream) {
+                  void* workspace, const DecodePlan& plan, hipStream_t stream, const AppendRows* append) {
   DecodeParams prm;
+  prm.k_new = append ? append->k_new : nullptr;
+  prm.v_new = append ? append->v_new : nullptr;
+  prm.k_w = append ? append->k : nullptr;
+  prm.v_w = append ? append->v : nullptr;
+  prm.ks_w = append ? append->k_scale : nullptr;
+  prm.vs_w = append ? append->v_scale : nullptr;
   prm.q = q;
   prm.k = kv.k;
   prm.v = kv.v;

@@ -34,17 +34,11 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, kWave));
 
-  const float s = a / 127.0f;            // correctly rounded
+  const float s = kv_row_scale(a);
   uint32_t packed = 0;
-  if (s != 0.0f) {
-    const float v[4] = {x.x, x.y, x.z, x.w};
+  const float v[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float qv = rintf(v[i] / s);        // correctly rounded, ties to even
-      qv = fminf(fmaxf(qv, -127.0f), 127.0f);
-      packed |= ((uint32_t)(int32_t)qv & 0xffu) << (8 * i);
-    }
-  }
+  for (int i = 0; i < 4; ++i) packed |= ((uint32_t)kv_code(v[i], s) & 0xffu) << (8 * i);
   if (!live) return;
   const int64_t pos = (int64_t)start_pos[b] + t;
   if (pos < 0 || pos >= L_cap) return;

@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert {"kv_quantize_int8", "mqa_decode", "mqa_prefill_chunk", "mqa_decode_workspace_bytes",
-            "mqa_status_string"} <= set(names)
+    assert {"kv_quantize_int8", "mqa_decode", "mqa_decode_append", "mqa_prefill_chunk",
+            "mqa_decode_workspace_bytes", "mqa_status_string"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in mqa_int8.h but not exported"
 
@@ -125,3 +125,29 @@ def test_accounting_matches_oracle():
     for W in (0, 1024, 7):
         assert acct.prefill_pairs([8192] * 3 + [5], 512, W) == oracle.prefill_visible_pairs([8192] * 3 + [5], 512, W)
     assert acct.decode_kv_bytes(np.full(64, 4096), 0, 128) == 69_206_016
+
+
+def append(lib, **kw):
+    from mqa_attention_int8_amd.binding import mqa_kv_cache
+    a = dict(q=FAKE, kv=mqa_kv_cache(FAKE, FAKE, FAKE, FAKE, 64), kn=FAKE, vn=FAKE, seq=FAKE, max_len=64, B=2,
+             Hq=8, D=128, W=0, scale=0.1, out=FAKE, ws=None, ws_bytes=0)
+    a.update(kw)
+    v = a["kv"]
+    return lib.mqa_decode_append(a["q"], ctypes.byref(v) if v is not None else None, a["kn"], a["vn"], a["seq"],
+                                 a["max_len"], a["B"], a["Hq"], a["D"], a["W"], a["scale"], a["out"], a["ws"],
+                                 a["ws_bytes"], None)
+
+
+def test_decode_append_validation(lib):
+    """mqa_decode_append rejects bad arguments on the host, before any launch."""
+    assert append(lib, kn=None) == 1                 # MQA_ERR_NULL
+    assert append(lib, vn=None) == 1
+    assert append(lib, kv=None) == 1
+    assert append(lib, kn=FAKE + 2) == 4             # MQA_ERR_ALIGN (rows are fp32)
+    assert append(lib, D=96) == 3                    # MQA_ERR_UNSUPPORTED
+    assert append(lib, max_len=65) == 2              # MQA_ERR_SHAPE (beyond L_cap)
+    assert append(lib, B=0) == 2
+    from mqa_attention_int8_amd.binding import mqa_kv_cache
+    assert append(lib, kv=mqa_kv_cache(FAKE, FAKE, FAKE, FAKE, 62), max_len=60) == 4   # scales 4 at a time
+    # many partitions need a workspace
+    assert append(lib, B=8, max_len=60000, kv=mqa_kv_cache(FAKE, FAKE, FAKE, FAKE, 65536)) == 5

