@@ -2,10 +2,11 @@
 """Benchmark of MQA int8-KV decode on one MI355X.
 
 One step = one decode step of two attention layers that share ONE int8 KV
-buffer (cross-layer KV sharing): the new token's K and V rows are quantized
-into the buffer (kv_quantize_int8 x2), then a global layer and a
-sliding-window (1024) layer each run mqa_decode over it. Shapes: B = 64
-sequences of 4096 keys, 32 query heads, one KV head, head_dim 128.
+buffer (cross-layer KV sharing): the global layer owns the buffer and runs
+mqa_decode_append (the new token's K and V rows are encoded into it in the
+same launch), then the sliding-window (1024) layer runs mqa_decode over it.
+Shapes: B = 64 sequences of 4096 keys, 32 query heads, one KV head,
+head_dim 128.
 
 Inputs are synthetic (seeded N(0,1) on the device, K/V encoded with the
 library's own quantizer) and resident in HBM before timing. The step is
@@ -14,8 +15,8 @@ cannot serve the KV reads. Steps are captured in a HIP graph so the timing is
 the GPU's, not Python's.
 
 Prints ONE JSON line. ``value`` = decode tokens/s of the step (B tokens per
-step, attention only). ``roofline`` describes the global-layer mqa_decode
-call (partition kernel + merge kernel). ``cpu_baseline`` times the CPU oracle
+step, attention only). ``roofline`` describes the global-layer call
+(partition kernel with the fused append + merge kernel). ``cpu_baseline`` times the CPU oracle
 on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -113,7 +114,6 @@ def bench_decode(torch, m, acct, args, stream):
     gen.manual_seed(2)
     bufs = make_decode_buffers(torch, m, B, L, D, R, gen)
     seq_lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
-    start_pos = seq_lens - 1
     q = [[torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in windows]
          for _ in range(R)]
     knew = [torch.randn((B, 1, D), generator=gen, device="cuda") for _ in range(R)]
@@ -122,11 +122,11 @@ def bench_decode(torch, m, acct, args, stream):
     ws = [m.decode_workspace(B, Hq, D, L, w) for w in windows]
 
     def one_step(r):
+        # the global layer owns the buffer: it appends the new token (fused), the window layer reads it
         kv = bufs[r]
-        m.kv_quantize_int8(knew[r], kv.k, kv.k_scale, start_pos)
-        m.kv_quantize_int8(vnew[r], kv.v, kv.v_scale, start_pos)
-        for li, w in enumerate(windows):
-            m.mqa_decode(q[r][li], kv, seq_lens, L, w, out=outs[li], workspace=ws[li])
+        m.mqa_decode_append(q[r][0], kv, knew[r].view(B, D), vnew[r].view(B, D), seq_lens, L, windows[0],
+                            out=outs[0], workspace=ws[0])
+        m.mqa_decode(q[r][1], kv, seq_lens, L, windows[1], out=outs[1], workspace=ws[1])
 
     def period():
         for r in range(R):
@@ -134,7 +134,8 @@ def bench_decode(torch, m, acct, args, stream):
 
     def global_only():
         for r in range(R):
-            m.mqa_decode(q[r][0], bufs[r], seq_lens, L, 0, out=outs[0], workspace=ws[0])
+            m.mqa_decode_append(q[r][0], bufs[r], knew[r].view(B, D), vnew[r].view(B, D), seq_lens, L, 0,
+                                out=outs[0], workspace=ws[0])
 
     with torch.cuda.stream(stream):
         for _ in range(max(1, args.warmup // R)):
@@ -145,7 +146,7 @@ def bench_decode(torch, m, acct, args, stream):
         ms, _ = run_steps(torch, period, reps, use_graph, stream)
         steps_done = reps * R
         ms_step = ms / steps_done
-        # dominant kernel: the global layer's mqa_decode (partition + merge)
+        # dominant kernel: the global layer's call (fused append + partitions, then the merge)
         ms_g, _ = run_steps(torch, global_only, reps, use_graph, stream)
         ms_call = ms_g / (reps * R)
     kv_step = sum(acct.decode_kv_bytes([L] * B, w, D) for w in windows)
@@ -174,10 +175,9 @@ def bench_hybrid(torch, m, acct, stream):
     gen.manual_seed(3)
     bufs = {name: make_decode_buffers(torch, m, B, L_cap, D, 1, gen)[0] for name in ("G", "A", "Bf")}
     seq_lens = torch.from_numpy(lens).cuda()
-    start_pos = seq_lens - 1
     q = [torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in w.layers]
-    knew = torch.randn((B, 1, D), generator=gen, device="cuda")
-    vnew = torch.randn((B, 1, D), generator=gen, device="cuda")
+    knew = torch.randn((B, D), generator=gen, device="cuda")
+    vnew = torch.randn((B, D), generator=gen, device="cuda")
     out = torch.empty((B, Hq, D), device="cuda")
     ws = torch.zeros(max(m.mqa_decode_workspace_bytes(B, Hq, D, L, win) for _, win in w.layers) + 16,
                      dtype=torch.uint8, device="cuda")
@@ -188,9 +188,10 @@ def bench_hybrid(torch, m, acct, stream):
     def block():
         for li, (name, win) in enumerate(w.layers):
             kv = bufs[name]
-            if owners[name] == li:             # first layer of a sharing group writes the token
-                m.append_kv(kv, knew, vnew, start_pos)
-            m.mqa_decode(q[li], kv, seq_lens, L, win, out=out, workspace=ws)
+            if owners[name] == li:             # first layer of a sharing group writes the token (fused)
+                m.mqa_decode_append(q[li], kv, knew, vnew, seq_lens, L, win, out=out, workspace=ws)
+            else:
+                m.mqa_decode(q[li], kv, seq_lens, L, win, out=out, workspace=ws)
 
     with torch.cuda.stream(stream):
         for _ in range(3):
@@ -353,7 +354,7 @@ def main():
     line = {
         "metric": METRIC, "value": dec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": dec["steps_done"], "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": "decode_B64_Hq32_D128_L4096: append + global layer + window-1024 layer "
                                "sharing one int8 KV buffer",
@@ -362,7 +363,7 @@ def main():
         "kv_read_GBps": dec["step_kv_GBps"], "kv_read_frac_hbm_peak": dec["step_kv_GBps"] / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": counted_traffic(),
-                     "kernel": "mqa_decode global layer (decode_partition_kernel + decode_merge_kernel)",
+                     "kernel": "global layer: mqa_decode_append (decode_partition_kernel + decode_merge_kernel)",
                      "algorithmic_bytes_per_launch": dec["global_kv_bytes"],
                      "avg_launch_us": dec["global_call_us"]},
         "cpu_baseline": cpu,

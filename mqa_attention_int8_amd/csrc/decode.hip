@@ -330,6 +330,60 @@ __device__ __forceinline__ void patch_new_row(Tile<D>& t, const int8_t* nk, cons
       }
 }
 
+// Fused append, done by the wave that draws the tile holding the new key
+// (row r of the tile): it encodes the new K and V rows (lane holds elements
+// [D/64 * lane, D/64 * (lane + 1)) of each in xk, xv) with the same arithmetic
+// as kv_quantize_int8, writes them to the cache row (first head group only),
+// and patches the tile registers, which may hold what the cache had before.
+template <int D>
+__device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D / 64], const float (&xv)[D / 64],
+                                               int8_t* scratch, int r, int g, int c, int lane, bool write,
+                                               int8_t* krow, int8_t* vrow, float* ks, float* vs) {
+  constexpr int E = D / 64;  // elements per lane
+  float ak = 0.f, av = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    ak = fmaxf(ak, fabsf(xk[e]));
+    av = fmaxf(av, fabsf(xv[e]));
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    ak = wave_max_xor(ak, m);
+    av = wave_max_xor(av, m);
+  }
+  const float sk = kv_row_scale(ak), sv = kv_row_scale(av);
+  uint32_t ck = 0, cv = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    ck |= ((uint32_t)kv_code(xk[e], sk) & 0xffu) << (8 * e);
+    cv |= ((uint32_t)kv_code(xv[e], sv) & 0xffu) << (8 * e);
+  }
+  // the codes in order in the wave's LDS scratch: K at [0, D), V at [D, 2D)
+  if constexpr (E == 2) {
+    reinterpret_cast<uint16_t*>(scratch)[lane] = (uint16_t)ck;
+    reinterpret_cast<uint16_t*>(scratch + D)[lane] = (uint16_t)cv;
+    if (write) {
+      reinterpret_cast<uint16_t*>(krow)[lane] = (uint16_t)ck;
+      reinterpret_cast<uint16_t*>(vrow)[lane] = (uint16_t)cv;
+    }
+  } else {
+    scratch[lane] = (int8_t)ck;
+    scratch[D + lane] = (int8_t)cv;
+    if (write) {
+      krow[lane] = (int8_t)ck;
+      vrow[lane] = (int8_t)cv;
+    }
+  }
+  if (write && lane == 0) {
+    *ks = sk;
+    *vs = sv;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  const float ns[2] = {sk, sv};
+  patch_new_row<D>(t, scratch, ns, r, g, c);
+}
+
 // The work-group's tiles pt0 + [0, count) are handed out to its waves from an
 // LDS counter, so waves that run ahead (the SIMDs favour older waves) take
 // more tiles and all finish close together. Which wave sums which tile then
@@ -341,7 +395,9 @@ template <int D, int NT>
 __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D, NT>& st, const SeqBuffers& sb,
                                           const TileOffsets& off, const f16x8 (&qop)[NT][D / 32], float kscale,
                                           int pt0, int count, int ia, int ib, int* next, int lane, int lo, int hi,
-                                          int g, int new_tile, const int8_t* nk, const float* ns) {
+                                          int g, int new_tile, const float (&xk)[D / 64], const float (&xv)[D / 64],
+                                          int8_t* scratch, bool write, int8_t* krow, int8_t* vrow, float* ks,
+                                          float* vs) {
   const int c = lane & 15;
   const auto grab = [&]() {
     int r = 0;
@@ -351,12 +407,14 @@ __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D,
   // ia < ib at the top of the loop and handed-out indices only grow, so once
   // ia is past the end so is ib (and vice versa in the middle).
   while (ia < count) {
-    if (ia == new_tile) patch_new_row<D>(ta, nk, ns, hi - 1 - (pt0 + ia) * kTileKeys, g, c);
+    if (ia == new_tile)
+      encode_new_row<D>(ta, xk, xv, scratch, hi - 1 - (pt0 + ia) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
     compute_tile<D, NT>(ta, st, qop, kscale, (pt0 + ia) * kTileKeys, lo, hi, g);
     ia = grab();
     load_tile<D>(ta, sb, off, (pt0 + ia) * kTileKeys, ia < count);
     if (ib >= count) break;
-    if (ib == new_tile) patch_new_row<D>(tb, nk, ns, hi - 1 - (pt0 + ib) * kTileKeys, g, c);
+    if (ib == new_tile)
+      encode_new_row<D>(tb, xk, xv, scratch, hi - 1 - (pt0 + ib) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
     compute_tile<D, NT>(tb, st, qop, kscale, (pt0 + ib) * kTileKeys, lo, hi, g);
     ib = grab();
     load_tile<D>(tb, sb, off, (pt0 + ib) * kTileKeys, ib < count);
@@ -381,9 +439,7 @@ void decode_partition_kernel(DecodeParams p) {
   __shared__ float sm_m[WV][HP];
   __shared__ float sm_l[WV][HP];
   __shared__ int sm_next;  // next tile (relative to pt0) to hand out
-  __shared__ __attribute__((aligned(16))) int8_t sm_new[2 * D];  // fused append: encoded K, V row
-  __shared__ float sm_news[2];                                   // ... and its two scales
-  __shared__ float sm_amax[WV];
+  __shared__ __attribute__((aligned(16))) int8_t sm_new[WV][2 * D];  // fused append: per-wave scratch
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -427,11 +483,14 @@ void decode_partition_kernel(DecodeParams p) {
         qraw[nt][kk] = buf_load16(qr, (uint32_t)(((16 * nt + c) * D + g * (D / 4) + 8 * kk) * 2), 0);
   }
   const int n_raw = p.seq_lens[b];
-  // fused append: thread x < D holds k_new[b][x], D <= x < 2D holds v_new[b][x - D]
+  // fused append: lane holds elements [D/64 * lane, D/64 * (lane + 1)) of the new K and V rows
   const bool appending = p.k_new != nullptr;
-  float xnew = 0.f;
-  if (appending && threadIdx.x < 2 * D)
-    xnew = threadIdx.x < D ? p.k_new[(int64_t)b * D + threadIdx.x] : p.v_new[(int64_t)b * D + threadIdx.x - D];
+  float xk[D / 64], xv[D / 64];
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) {
+    xk[e] = appending ? p.k_new[(int64_t)b * D + (D / 64) * lane + e] : 0.f;
+    xv[e] = appending ? p.v_new[(int64_t)b * D + (D / 64) * lane + e] : 0.f;
+  }
   __builtin_amdgcn_s_waitcnt(0);
 
   int n = __builtin_amdgcn_readfirstlane(n_raw);  // same for the whole work-group
@@ -443,39 +502,9 @@ void decode_partition_kernel(DecodeParams p) {
   const int pt0 = t_begin + part * tpp;
   const int pt1 = min(pt0 + tpp, t_end);
   const int count = pt1 - pt0;  // tiles of this partition (may be <= 0)
-  // Fused append: the work-group whose range holds row n - 1 encodes the new
-  // row (the same arithmetic as kv_quantize_int8), writes it to the cache and
-  // keeps it in LDS for the wave that computes that tile.
-  int new_tile = -1;
-  if (appending && n > 0 && (n - 1) / kTileKeys >= pt0 && (n - 1) / kTileKeys < pt1) {
-    new_tile = (n - 1) / kTileKeys - pt0;
-    float a = fabsf(xnew);
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, kWave));
-    if (lane == 0) sm_amax[wave] = a;
-    __syncthreads();
-    const int tw = (int)threadIdx.x < D ? 0 : 1;  // tensor of this thread: K or V
-    float amax = 0.f;
-    for (int w = tw * (D / 64); w < (tw + 1) * (D / 64); ++w) amax = fmaxf(amax, sm_amax[w]);
-    const float sc = kv_row_scale(amax);
-    if (threadIdx.x < 2 * D) {
-      const int8_t code = (int8_t)kv_code(xnew, sc);
-      sm_new[threadIdx.x] = code;
-      const int64_t row = (int64_t)b * p.L_cap + (n - 1);
-      if (blockIdx.z != 0) {
-        // another head group writes the row; this one only needs it in LDS
-        if (threadIdx.x == 0) sm_news[0] = sc;
-        if (threadIdx.x == D) sm_news[1] = sc;
-      } else if (tw == 0) {
-        p.k_w[row * D + threadIdx.x] = code;
-        if (threadIdx.x == 0) { p.ks_w[row] = sc; sm_news[0] = sc; }
-      } else {
-        p.v_w[row * D + threadIdx.x - D] = code;
-        if (threadIdx.x == D) { p.vs_w[row] = sc; sm_news[1] = sc; }
-      }
-    }
-    __syncthreads();
-  }
+  // Fused append: the wave that draws the tile holding row n - 1 encodes it.
+  const int new_tile = (appending && n > 0) ? (n - 1) / kTileKeys - pt0 : -1;  // outside [0, count): none here
+  const int64_t new_row = (int64_t)b * p.L_cap + (n > 0 ? n - 1 : 0);
   Tile<D> ta, tb;
   load_tile<D>(ta, sb, off, (pt0 + wave) * kTileKeys, wave < count);
   load_tile<D>(tb, sb, off, (pt0 + wave + WV) * kTileKeys, wave + WV < count);
@@ -523,7 +552,8 @@ void decode_partition_kernel(DecodeParams p) {
   st.vexp = -1000;
 
   run_tiles<D, NT>(ta, tb, st, sb, off, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g,
-                   new_tile, sm_new, sm_news);
+                   new_tile, xk, xv, sm_new[wave], blockIdx.z == 0, p.k_w + new_row * D, p.v_w + new_row * D,
+                   p.ks_w + new_row, p.vs_w + new_row);
 
   // ---- combine the waves of the work-group -----------------------------------
   // Each wave parks its raw accumulators and (m, l) per head in LDS (lane-ordered
