@@ -155,10 +155,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-__device__ __forceinline__ float wave_max_xor(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, kWave));
-}
-
 // Max of 8 values as a chain the compiler turns into v_max3_f32.
 __device__ __forceinline__ float max8(const float (&x)[8]) {
   float m = fmaxf(fmaxf(x[0], x[1]), x[2]);
@@ -179,6 +175,19 @@ __device__ __forceinline__ int quad_max_i(int v) {
   v = max((int)a[0], (int)a[1]);
   const auto b = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
   return max((int)b[0], (int)b[1]);
+}
+// Max over all 64 lanes, in every lane: two lane-half swaps, then rotations
+// within each row of 16 lanes and quad permutations (DPP, no LDS traffic).
+__device__ __forceinline__ float wave_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));  // row_ror:8
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));  // row_ror:4
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false)));   // quad [2,3,0,1]
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false)));   // quad [1,0,3,2]
+  return v;
 }
 __device__ __forceinline__ float quad_sum(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -203,6 +212,17 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t vo
 }
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+// Streaming variants: the non-temporal hint (nt) for data read once per call.
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT));
+}
+__device__ __forceinline__ u32x2 buf_load8_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kCachePolicyNT));
+}
+__device__ __forceinline__ uint32_t buf_load4_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kCachePolicyNT);
 }
 
 }  // namespace mqa

@@ -11,33 +11,39 @@
 //
 // Design for gfx950 (decode is bound by HBM reads of the cache):
 //  * One work-group = one sequence x one contiguous range of 32-key tiles
-//    (a "partition"), ALL query heads. Each K/V byte is read from HBM once
-//    per call and feeds every head: this is where MQA's reuse lives.
-//  * Per 32-key tile a wave runs S^T = K Q^T and O^T += V^T P'^T on bf16
-//    MFMA (v_mfma_f32_16x16x32_bf16): 32 heads x 128 dims x 2 flops per key
+//    (a "partition") x up to 32 query heads (more heads: more head groups
+//    in grid z). Each K/V byte is read from HBM once per call and head group
+//    and feeds all its heads: this is where MQA's reuse lives.
+//  * Eight waves per work-group, one work-group per compute unit. The
+//    work-group's tiles are handed to its waves from an LDS counter, so the
+//    waves finish together whatever the SIMD arbiter favours (which wave sums
+//    which tile, and so the last bits of the result, depends on timing).
+//  * Per 32-key tile a wave runs S^T = K Q^T and O^T += V^T P''^T on fp16
+//    MFMA (v_mfma_f32_16x16x32_f16): 32 heads x 128 dims x 2 flops per key
 //    per product is far above what the vector ALUs can sustain at HBM rate.
-//  * int8 -> bf16 is exact and costs one instruction per element (an SDWA
-//    sign-extended byte convert) plus one permute per pair.
+//  * int8 -> fp16 is exact and costs one instruction per element (an SDWA
+//    sign-extended byte convert). q is scaled per wave by a power of two into
+//    fp16's top binade; the scale is folded into the per-key logit factor.
 //  * The contraction index d is permuted consistently in Q and K so that a
 //    lane's K bytes are one contiguous run of a key row; the key index is
-//    permuted consistently in P' and V so that the accumulator layout of S^T
+//    permuted consistently in P'' and V so that the accumulator layout of S^T
 //    is directly the B operand of the PV product (no shuffles), and V's
 //    column mapping makes each lane's V bytes contiguous within a row.
-//  * P' = p * s_v is split into bf16 hi + lo parts (two MFMAs), so the PV
-//    product carries ~16 significant bits instead of 8.
-//  * Loads are software-pipelined: the next tile's K, V and scales are in
-//    flight while the current tile is computed.
-//  * Online softmax (running max m, sum l, rescaled accumulator) in the log2
-//    domain per head, rescaling only when the max grows by more than 2^8.
-//    The 4 waves of a work-group merge through LDS. With several partitions
-//    per sequence, each work-group writes its (m, l, o) state and a small
-//    second kernel combines them with a log-sum-exp merge (workshop
-//    transcript 00:48:02-00:49:13: tiles plus three running quantities give
-//    the exact softmax). A kernel boundary is the cheap way to make the
-//    states written on one XCD visible to another; an in-kernel hand-off
-//    needs an L2 write-back per work-group.
+//  * P'' (below) is split into fp16 hi + lo parts (two MFMAs), so the PV
+//    product carries 22 significant bits instead of 11.
+//  * Loads are software-pipelined: two tiles per wave in registers, one being
+//    computed while the other is in flight.
+//  * Online softmax (running offset m, sum l, rescaled accumulator) in the
+//    log2 domain per head. The waves of a work-group combine through LDS.
+//    With several partitions per sequence, each work-group writes its
+//    normalised (m, l, o) state and a small second kernel combines them with
+//    a log-sum-exp merge (workshop transcript 00:48:02-00:49:13: tiles plus
+//    three running quantities give the exact softmax). A kernel boundary is
+//    the cheap way to make the states written on one XCD visible to another.
 //  * Tiles wholly outside the window are never loaded; only the tiles that
 //    straddle a window end are masked per key.
+//  * Optionally (mqa_decode_append) the wave that draws the tile holding the
+//    sequence's last row first encodes the new token's K and V into it.
 #include <math.h>
 
 #include "common.h"
@@ -131,23 +137,25 @@ __device__ __forceinline__ void load_tile(Tile<D>& t, const SeqBuffers& sb, cons
     off.s = kNowhere;
     base = 0;
   }
-  // scalar offsets of the tile's first row (base is wave-uniform)
+  // scalar offsets of the tile's first row (base is wave-uniform). K and V
+  // are read once per call: non-temporal loads (measured faster); the
+  // scales keep the default policy.
   const uint32_t kv_s = __builtin_amdgcn_readfirstlane((uint32_t)base * D);
   const uint32_t sc_s = __builtin_amdgcn_readfirstlane((uint32_t)base * 4);
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int w = 0; w < Tile<D>::KV4; ++w) t.k[hf][w] = buf_load16(sb.k, off.k + hf * 16 * D + 16 * w, kv_s);
+    for (int w = 0; w < Tile<D>::KV4; ++w) t.k[hf][w] = buf_load16_nt(sb.k, off.k + hf * 16 * D + 16 * w, kv_s);
   // key slot i: key base + 16(i/4) + 4g + i%4
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t o = off.v + (16 * (i >> 2) + (i & 3)) * D;
     if constexpr (Tile<D>::VW == 2) {
-      const u32x2 x = buf_load8(sb.v, o, kv_s);
+      const u32x2 x = buf_load8_nt(sb.v, o, kv_s);
       t.v[i][0] = x[0];
       t.v[i][1] = x[1];
     } else {
-      t.v[i][0] = buf_load4(sb.v, o, kv_s);
+      t.v[i][0] = buf_load4_nt(sb.v, o, kv_s);
     }
   }
 #pragma unroll
@@ -346,11 +354,8 @@ __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D /
     ak = fmaxf(ak, fabsf(xk[e]));
     av = fmaxf(av, fabsf(xv[e]));
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    ak = wave_max_xor(ak, m);
-    av = wave_max_xor(av, m);
-  }
+  ak = wave_max(ak);
+  av = wave_max(av);
   const float sk = kv_row_scale(ak), sv = kv_row_scale(av);
   uint32_t ck = 0, cv = 0;
 #pragma unroll
@@ -447,8 +452,6 @@ void decode_partition_kernel(DecodeParams p) {
   const int c = lane & 15;
   const int b = blockIdx.y;
   const int part = blockIdx.x;
-  if (threadIdx.x == 0) sm_next = 2 * WV;
-  __syncthreads();
   const int Hq = p.Hq;                     // heads of the layer (row stride of q and out)
   const int h0 = kHeadsPerGroup * (int)blockIdx.z;   // first head of this group
   const int Hg = min(Hq - h0, NT * 16);    // heads of this group
@@ -467,12 +470,19 @@ void decode_partition_kernel(DecodeParams p) {
   off.v = (uint32_t)(4 * g * D + (D / 16) * c);
   off.s = (uint32_t)(16 * g);
 
-  // Loads go out first: the q rows this lane needs and the sequence length
-  // (small, needed first); they are waited for while the memory system is
-  // still idle, since behind the tile stream they would return only once most
-  // of the chip-wide first burst of tile loads had drained. Lane (g, c) takes
+  // Loads go out first: the sequence length, the q rows this lane needs and
+  // the new K/V row elements (fused append). A compute unit's vector memory
+  // requests are served in order, so every wave issues these before any wave
+  // of the work-group issues a tile load (the barrier orders issue, it does
+  // not wait for data): behind the tile stream they would return only after
+  // most of the unit's first burst of tile loads. They are then waited for
+  // while the first tile is in flight. Lane (g, c) takes
   // q[h = 16nt + c][d = g*D/4 + 8kk + 0..7] (bf16), loaded unconditionally
   // through a buffer resource (heads past Hq read as zero).
+  // The length goes through the vector memory path: a scalar load would be
+  // waited for at the barrier below (it shares a counter with the LDS write
+  // before it).
+  const int n_raw = (int)buf_load4(make_rsrc(p.seq_lens + b, 4), 0, 0);
   u32x4 qraw[NT][KK];
   {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + ((int64_t)b * Hq + h0) * D, (uint32_t)(Hg * D * 2));
@@ -482,7 +492,6 @@ void decode_partition_kernel(DecodeParams p) {
       for (int kk = 0; kk < KK; ++kk)
         qraw[nt][kk] = buf_load16(qr, (uint32_t)(((16 * nt + c) * D + g * (D / 4) + 8 * kk) * 2), 0);
   }
-  const int n_raw = p.seq_lens[b];
   // fused append: lane holds elements [D/64 * lane, D/64 * (lane + 1)) of the new K and V rows
   const bool appending = p.k_new != nullptr;
   float xk[D / 64], xv[D / 64];
@@ -491,7 +500,17 @@ void decode_partition_kernel(DecodeParams p) {
     xk[e] = appending ? p.k_new[(int64_t)b * D + (D / 64) * lane + e] : 0.f;
     xv[e] = appending ? p.v_new[(int64_t)b * D + (D / 64) * lane + e] : 0.f;
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  if (threadIdx.x == 0) sm_next = 2 * WV;
+  __syncthreads();
+
+  // A global layer's first tile per wave does not depend on the sequence
+  // length: it is loaded before the length arrives (beyond the cache capacity
+  // buffer loads return zero; a tile past the length is never computed).
+  // A windowed layer needs the length to place its tiles. (Issuing the second
+  // tile this early too measured slower: the first work-groups' loads then
+  // delay the q loads of those dispatched last.)
+  Tile<D> ta, tb;
+  if (!WINDOWED) load_tile<D>(ta, sb, off, (part * tpp + wave) * kTileKeys, wave < tpp);
 
   int n = __builtin_amdgcn_readfirstlane(n_raw);  // same for the whole work-group
   n = n < 0 ? 0 : (n > p.L_cap ? p.L_cap : n);
@@ -505,8 +524,7 @@ void decode_partition_kernel(DecodeParams p) {
   // Fused append: the wave that draws the tile holding row n - 1 encodes it.
   const int new_tile = (appending && n > 0) ? (n - 1) / kTileKeys - pt0 : -1;  // outside [0, count): none here
   const int64_t new_row = (int64_t)b * p.L_cap + (n > 0 ? n - 1 : 0);
-  Tile<D> ta, tb;
-  load_tile<D>(ta, sb, off, (pt0 + wave) * kTileKeys, wave < count);
+  if (WINDOWED) load_tile<D>(ta, sb, off, (pt0 + wave) * kTileKeys, wave < count);
   load_tile<D>(tb, sb, off, (pt0 + wave + WV) * kTileKeys, wave + WV < count);
 
   // Q^T as the B operand in fp16: the wave scales q by an exact power of two
@@ -523,8 +541,7 @@ void decode_partition_kernel(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo_to_f32(qraw[nt][kk][e])), fabsf(bf16_hi_to_f32(qraw[nt][kk][e]))));
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) qmax = wave_max_xor(qmax, m);
+    qmax = wave_max(qmax);
     int eq = qmax > 0.f ? __builtin_amdgcn_frexp_expf(qmax) : 0;  // qmax < 2^eq
     eq = eq < -100 ? -100 : eq;
     const float qup = __builtin_ldexpf(1.f, 15 - eq);
