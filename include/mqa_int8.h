@@ -34,8 +34,9 @@
  *    kernel.
  *  - bf16 values are passed as their 16-bit patterns (uint16_t).
  *  - Device-resident lengths (seq_lens, prefix_lens, start_pos) are trusted
- *    data: kernels clamp them into the cache so that no access leaves the
- *    buffers, but results for out-of-range values are unspecified.
+ *    data: kernels clamp them into the cache (and prefix_lens to
+ *    max_prefix_len) so that no access leaves the buffers or the workspace,
+ *    but results for out-of-range values are unspecified.
  *  - Supported shapes: head_dim D in {64, 128}; 1 <= Hq <= 64 query heads;
  *    B >= 1. Validation happens before any HIP call, so bad arguments are
  *    reported without touching the device.
@@ -182,6 +183,91 @@ int mqa_prefill_chunk(const uint16_t* q, const mqa_kv_view* kv,
                       int32_t B, int32_t C, int32_t Hq, int32_t D,
                       int32_t window, float softmax_scale, float* out,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Paged KV buffers: the same operations on a cache kept in fixed-size blocks.
+ * [tubrief.io workshop transcript 01:01:35-01:03:22: instead of one
+ * contiguous region per request, the KV of a sequence is logically contiguous
+ * but lives in blocks of a shared pool, mapped through a table and allocated
+ * as tokens arrive.] A table shorter than a sequence wraps around: the buffer
+ * then keeps only the most recent positions, which is all a sliding-window
+ * layer reads [9c1h.cn page "秘訣1", hybrid attention horizon item: local
+ * layers attend to the last 1024 tokens], so a window-only buffer needs
+ * memory proportional to the window, not to the sequence.
+ *
+ * Token position t of sequence b lives at pool row
+ *     r = block_table[b * table_len + (t / block_size) % table_len]
+ *             * block_size + t % block_size,
+ * i.e. K bytes k[r * D .. r * D + D), its scale k_scale[r] (same for V).
+ * Table entries outside [0, num_blocks) are clamped into the pool by the
+ * kernels (so no access leaves it), but then give unspecified results.
+ * Requirements checked by the entry points: block_size a power of two in
+ * [32, 4096]; table_len, num_blocks >= 1; pools 16-byte aligned; whenever a
+ * call may reach positions >= table_len * block_size (the table wraps), the
+ * layer must be windowed and the keys it reads still resident (see each
+ * function).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int8_t* k;                  /* pool, int8 [num_blocks, block_size, D] */
+  int8_t* v;                  /* pool, int8 [num_blocks, block_size, D] */
+  float* k_scale;             /* pool, fp32 [num_blocks, block_size]    */
+  float* v_scale;             /* pool, fp32 [num_blocks, block_size]    */
+  const int32_t* block_table; /* int32 [B, table_len] (device)          */
+  int32_t block_size;
+  int32_t table_len;
+  int32_t num_blocks;
+} mqa_kv_paged;
+
+/* kv_quantize_int8_paged - kv_quantize_int8 for K and V of a paged buffer in
+ * one launch: rows start_pos[b] .. start_pos[b]+T-1 of sequence b, with the
+ * same encoding, go to their pool rows. k_src, v_src fp32 [B, T, D] (16-byte
+ * aligned). Negative positions are skipped. T <= table_len * block_size (a
+ * call never writes one pool row twice). Errors: NULL, SHAPE, UNSUPPORTED,
+ * ALIGN, HIP. */
+int kv_quantize_int8_paged(const float* k_src, const float* v_src,
+                           const mqa_kv_paged* kv, const int32_t* start_pos,
+                           int32_t B, int32_t T, int32_t D, void* stream);
+
+/* Workspace of mqa_decode_paged / mqa_decode_append_paged (0 for a single
+ * pass or invalid arguments). */
+size_t mqa_decode_paged_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
+                                        int32_t max_seq_len, int32_t window,
+                                        int32_t block_size);
+
+/* mqa_decode_paged - mqa_decode over a paged buffer; arguments, output and
+ * errors as mqa_decode. Positions t and t + table_len * block_size share a
+ * pool row, so a wrapping table keeps exactly the last table_len * block_size
+ * positions written (in order). If max_seq_len > table_len * block_size the
+ * layer must therefore be windowed with window <= table_len * block_size. */
+int mqa_decode_paged(const uint16_t* q, const mqa_kv_paged* kv,
+                     const int32_t* seq_lens, int32_t max_seq_len, int32_t B,
+                     int32_t Hq, int32_t D, int32_t window,
+                     float softmax_scale, float* out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* mqa_decode_append_paged - mqa_decode_append over a paged buffer: the new
+ * token's K and V go to the pool row of position seq_lens[b] - 1. Same
+ * arguments and requirements as mqa_decode_paged plus k_new, v_new as in
+ * mqa_decode_append. */
+int mqa_decode_append_paged(const uint16_t* q, const mqa_kv_paged* kv,
+                            const float* k_new, const float* v_new,
+                            const int32_t* seq_lens, int32_t max_seq_len,
+                            int32_t B, int32_t Hq, int32_t D, int32_t window,
+                            float softmax_scale, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* mqa_prefill_chunk_paged - mqa_prefill_chunk over a paged buffer (the
+ * chunk's own K/V written first with kv_quantize_int8_paged); workspace as
+ * mqa_prefill_workspace_bytes. If max_prefix_len + C > table_len *
+ * block_size the layer must be windowed with
+ * window + C - 1 <= table_len * block_size, so that every key the chunk
+ * reads is still in the pool after the chunk was written. */
+int mqa_prefill_chunk_paged(const uint16_t* q, const mqa_kv_paged* kv,
+                            const int32_t* prefix_lens, int32_t max_prefix_len,
+                            int32_t B, int32_t C, int32_t Hq, int32_t D,
+                            int32_t window, float softmax_scale, float* out,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mqa_status_string(int status);

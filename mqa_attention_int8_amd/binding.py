@@ -40,6 +40,12 @@ class mqa_kv_cache(ctypes.Structure):
                 ("v_scale", ctypes.c_void_p), ("L_cap", ctypes.c_int32)]
 
 
+class mqa_kv_paged(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+                ("table_len", ctypes.c_int32), ("num_blocks", ctypes.c_int32)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -71,6 +77,19 @@ def load_library() -> ctypes.CDLL:
         lib.mqa_prefill_chunk.argtypes = [vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32,
                                           i32, f32, vp, vp, ctypes.c_size_t, vp]
         lib.mqa_prefill_chunk.restype = ctypes.c_int
+        pg = ctypes.POINTER(mqa_kv_paged)
+        lib.kv_quantize_int8_paged.argtypes = [vp, vp, pg, vp, i32, i32, i32, vp]
+        lib.kv_quantize_int8_paged.restype = ctypes.c_int
+        lib.mqa_decode_paged_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        lib.mqa_decode_paged_workspace_bytes.restype = ctypes.c_size_t
+        lib.mqa_decode_paged.argtypes = [vp, pg, vp, i32, i32, i32, i32, i32, f32, vp, vp, ctypes.c_size_t, vp]
+        lib.mqa_decode_paged.restype = ctypes.c_int
+        lib.mqa_decode_append_paged.argtypes = [vp, pg, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp,
+                                                ctypes.c_size_t, vp]
+        lib.mqa_decode_append_paged.restype = ctypes.c_int
+        lib.mqa_prefill_chunk_paged.argtypes = [vp, pg, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp,
+                                                ctypes.c_size_t, vp]
+        lib.mqa_prefill_chunk_paged.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -262,6 +281,135 @@ def mqa_prefill_chunk(q: torch.Tensor, kv: KVView, prefix_lens: torch.Tensor, ma
                                  C, Hq, D, int(window), scale, _ptr(out), _ptr(workspace), ws_bytes,
                                  _stream(stream)),
            "mqa_prefill_chunk")
+    return out
+
+
+class PagedKV:
+    """One paged KV buffer: int8 pools K/V [num_blocks, block_size, D], fp32
+    scale pools [num_blocks, block_size] and an int32 block table
+    [B, table_len] mapping logical block j of sequence b to pool block
+    table[b, j % table_len] (a short table makes a ring)."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                 block_table: torch.Tensor):
+        for t, n in ((k, "k"), (v, "v")):
+            _need(t, torch.int8, n, 3)
+        for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            _need(t, torch.float32, n, 2)
+        _need(block_table, torch.int32, "block_table", 2)
+        if k.shape != v.shape or k_scale.shape != v_scale.shape or tuple(k.shape[:2]) != tuple(k_scale.shape):
+            raise ValueError("inconsistent paged pool shapes")
+        self.k, self.v, self.k_scale, self.v_scale, self.block_table = k, v, k_scale, v_scale, block_table
+        self.num_blocks, self.block_size, self.D = (int(x) for x in k.shape)
+        self.B, self.table_len = (int(x) for x in block_table.shape)
+
+    @classmethod
+    def empty(cls, num_blocks: int, block_size: int, D: int, block_table: torch.Tensor, device="cuda"):
+        return cls(torch.zeros((num_blocks, block_size, D), dtype=torch.int8, device=device),
+                   torch.zeros((num_blocks, block_size, D), dtype=torch.int8, device=device),
+                   torch.zeros((num_blocks, block_size), dtype=torch.float32, device=device),
+                   torch.zeros((num_blocks, block_size), dtype=torch.float32, device=device),
+                   block_table)
+
+    def c_paged(self) -> mqa_kv_paged:
+        return mqa_kv_paged(self.k.data_ptr(), self.v.data_ptr(), self.k_scale.data_ptr(), self.v_scale.data_ptr(),
+                            self.block_table.data_ptr(), self.block_size, self.table_len, self.num_blocks)
+
+
+def kv_quantize_int8_paged(k_src: torch.Tensor, v_src: torch.Tensor, kv: PagedKV, start_pos: torch.Tensor,
+                           stream=None) -> None:
+    """Quantize new K and V rows (fp32 [B, T, D]) into their pool rows."""
+    lib = load_library()
+    _need(k_src, torch.float32, "k_src", 3)
+    _need(v_src, torch.float32, "v_src", 3)
+    _need(start_pos, torch.int32, "start_pos", 1)
+    B, T, D = (int(x) for x in k_src.shape)
+    if tuple(v_src.shape) != (B, T, D) or D != kv.D or start_pos.shape[0] != B or B > kv.B:
+        raise ValueError("kv_quantize_int8_paged: shape mismatch")
+    c = kv.c_paged()
+    _check(lib.kv_quantize_int8_paged(_ptr(k_src), _ptr(v_src), ctypes.byref(c), _ptr(start_pos), B, T, D,
+                                      _stream(stream)), "kv_quantize_int8_paged")
+
+
+def mqa_decode_paged_workspace_bytes(B: int, Hq: int, D: int, max_seq_len: int, window: int,
+                                     block_size: int) -> int:
+    return int(load_library().mqa_decode_paged_workspace_bytes(B, Hq, D, max_seq_len, window, block_size))
+
+
+def _paged_decode_args(q, kv, seq_lens, max_seq_len, window, softmax_scale, out, workspace):
+    _need(q, torch.bfloat16, "q", 3)
+    _need(seq_lens, torch.int32, "seq_lens", 1)
+    B, Hq, D = (int(x) for x in q.shape)
+    if B > kv.B or D != kv.D:
+        raise ValueError("paged decode: q does not match the buffer")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out", 3)
+    need = mqa_decode_paged_workspace_bytes(B, Hq, D, max_seq_len, window, kv.block_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
+    return B, Hq, D, out, workspace, ws_bytes, scale
+
+
+def mqa_decode_paged(q: torch.Tensor, kv: PagedKV, seq_lens: torch.Tensor, max_seq_len: int, window: int,
+                     softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mqa_decode over a paged buffer."""
+    lib = load_library()
+    B, Hq, D, out, workspace, ws_bytes, scale = _paged_decode_args(q, kv, seq_lens, max_seq_len, window,
+                                                                   softmax_scale, out, workspace)
+    c = kv.c_paged()
+    _check(lib.mqa_decode_paged(_ptr(q), ctypes.byref(c), _ptr(seq_lens), int(max_seq_len), B, Hq, D,
+                                int(window), scale, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
+           "mqa_decode_paged")
+    return out
+
+
+def mqa_decode_append_paged(q: torch.Tensor, kv: PagedKV, k_new: torch.Tensor, v_new: torch.Tensor,
+                            seq_lens: torch.Tensor, max_seq_len: int, window: int,
+                            softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mqa_decode_append over a paged buffer."""
+    lib = load_library()
+    B, Hq, D, out, workspace, ws_bytes, scale = _paged_decode_args(q, kv, seq_lens, max_seq_len, window,
+                                                                   softmax_scale, out, workspace)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, torch.float32, n, 2)
+        if tuple(t.shape) != (B, D):
+            raise ValueError(f"{n} must have shape {(B, D)}")
+    c = kv.c_paged()
+    _check(lib.mqa_decode_append_paged(_ptr(q), ctypes.byref(c), _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
+                                       int(max_seq_len), B, Hq, D, int(window), scale, _ptr(out),
+                                       _ptr(workspace), ws_bytes, _stream(stream)),
+           "mqa_decode_append_paged")
+    return out
+
+
+def mqa_prefill_chunk_paged(q: torch.Tensor, kv: PagedKV, prefix_lens: torch.Tensor, max_prefix_len: int,
+                            window: int, softmax_scale: float | None = None,
+                            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """mqa_prefill_chunk over a paged buffer."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q", 4)
+    _need(prefix_lens, torch.int32, "prefix_lens", 1)
+    B, C, Hq, D = (int(x) for x in q.shape)
+    if B > kv.B or D != kv.D:
+        raise ValueError("mqa_prefill_chunk_paged: q does not match the buffer")
+    if out is None:
+        out = torch.empty((B, C, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out", 4)
+    if workspace is None:
+        workspace = prefill_workspace(B, C, D, max_prefix_len, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
+    c = kv.c_paged()
+    _check(lib.mqa_prefill_chunk_paged(_ptr(q), ctypes.byref(c), _ptr(prefix_lens), int(max_prefix_len), B, C,
+                                       Hq, D, int(window), scale, _ptr(out), _ptr(workspace), ws_bytes,
+                                       _stream(stream)),
+           "mqa_prefill_chunk_paged")
     return out
 
 

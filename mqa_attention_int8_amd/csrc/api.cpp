@@ -54,6 +54,46 @@ int check_decode_shape(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len) {
   return MQA_OK;
 }
 
+// Validation of a paged buffer; fills the internal layout on success.
+int check_paged(const mqa_kv_paged* kv, mqa::KVLayout* layout) {
+  if (!kv || !kv->k || !kv->v || !kv->k_scale || !kv->v_scale || !kv->block_table) return MQA_ERR_NULL;
+  const int32_t bs = kv->block_size;
+  if (bs < 32 || bs > 4096 || (bs & (bs - 1)) != 0) return MQA_ERR_SHAPE;
+  if (kv->table_len <= 0 || kv->num_blocks <= 0) return MQA_ERR_SHAPE;
+  if ((int64_t)kv->num_blocks * bs > ((int64_t)1 << 40)) return MQA_ERR_SHAPE;
+  if (!aligned16(kv->k) || !aligned16(kv->v) || !aligned16(kv->k_scale) || !aligned16(kv->v_scale))
+    return MQA_ERR_ALIGN;
+  if (((uintptr_t)kv->block_table & 3u) != 0) return MQA_ERR_ALIGN;
+  int lb = 0;
+  while ((1 << lb) < bs) ++lb;
+  layout->table = kv->block_table;
+  layout->table_len = kv->table_len;
+  layout->log2_bs = lb;
+  layout->num_blocks = kv->num_blocks;
+  layout->L_cap = mqa::kPagedPositionLimit;
+  return MQA_OK;
+}
+
+// Keys a windowed layer reads are resident when the table wraps: position t
+// and t + table_len * block_size share a pool row, so the buffer holds
+// exactly the last table_len * block_size positions written, and the `span`
+// positions ending at the newest must fit in them.
+bool resident(const mqa_kv_paged* kv, int64_t max_pos_end, int32_t window, int64_t span) {
+  const int64_t cap = (int64_t)kv->table_len * kv->block_size;
+  if (max_pos_end <= cap) return true;
+  if (window <= 0) return false;
+  return span <= cap;
+}
+
+int check_decode_common(const uint16_t* q, const int32_t* seq_lens, const float* out, int32_t B, int32_t Hq,
+                        int32_t D, int32_t max_seq_len) {
+  if (!q || !seq_lens || !out) return MQA_ERR_NULL;
+  int st = check_decode_shape(B, Hq, D, max_seq_len);
+  if (st != MQA_OK) return st;
+  if (!aligned16(q) || !aligned16(out)) return MQA_ERR_ALIGN;
+  return MQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -105,8 +145,8 @@ int mqa_decode(const uint16_t* q, const mqa_kv_view* kv, const int32_t* seq_lens
     if (!workspace || workspace_bytes < plan.ws_bytes) return MQA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MQA_ERR_ALIGN;
   }
-  return mqa::launch_decode(q, *kv, seq_lens, B, Hq, D, window, softmax_scale, out, workspace, plan,
-                            static_cast<hipStream_t>(stream));
+  return mqa::launch_decode(q, *kv, mqa::KVLayout{}, seq_lens, B, Hq, D, window, softmax_scale, out, workspace,
+                            plan, static_cast<hipStream_t>(stream));
 }
 
 int mqa_decode_append(const uint16_t* q, const mqa_kv_cache* kv, const float* k_new, const float* v_new,
@@ -130,8 +170,8 @@ int mqa_decode_append(const uint16_t* q, const mqa_kv_cache* kv, const float* k_
     if (!aligned16(workspace)) return MQA_ERR_ALIGN;
   }
   const mqa::AppendRows rows{k_new, v_new, kv->k, kv->v, kv->k_scale, kv->v_scale};
-  return mqa::launch_decode(q, view, seq_lens, B, Hq, D, window, softmax_scale, out, workspace, plan,
-                            static_cast<hipStream_t>(stream), &rows);
+  return mqa::launch_decode(q, view, mqa::KVLayout{}, seq_lens, B, Hq, D, window, softmax_scale, out, workspace,
+                            plan, static_cast<hipStream_t>(stream), &rows);
 }
 
 size_t mqa_prefill_workspace_bytes(int32_t B, int32_t C, int32_t D, int32_t max_prefix_len) {
@@ -154,8 +194,99 @@ int mqa_prefill_chunk(const uint16_t* q, const mqa_kv_view* kv, const int32_t* p
   if (!workspace || workspace_bytes < mqa::prefill_workspace_bytes(B, C, D, max_prefix_len))
     return MQA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MQA_ERR_ALIGN;
-  return mqa::launch_prefill(q, *kv, prefix_lens, max_prefix_len, B, C, Hq, D, window,
+  return mqa::launch_prefill(q, *kv, mqa::KVLayout{}, prefix_lens, max_prefix_len, B, C, Hq, D, window,
                              softmax_scale, out, workspace, static_cast<hipStream_t>(stream));
+}
+
+int kv_quantize_int8_paged(const float* k_src, const float* v_src, const mqa_kv_paged* kv,
+                           const int32_t* start_pos, int32_t B, int32_t T, int32_t D, void* stream) {
+  if (!k_src || !v_src || !start_pos) return MQA_ERR_NULL;
+  mqa::KVLayout layout;
+  int st = check_paged(kv, &layout);
+  if (st != MQA_OK) return st;
+  if (B <= 0 || T <= 0 || D <= 0) return MQA_ERR_SHAPE;
+  if ((int64_t)T > (int64_t)kv->table_len * kv->block_size) return MQA_ERR_SHAPE;
+  if (!supported_d(D)) return MQA_ERR_UNSUPPORTED;
+  if (!aligned16(k_src) || !aligned16(v_src)) return MQA_ERR_ALIGN;
+  return mqa::launch_quantize_paged(k_src, v_src, kv->k, kv->v, kv->k_scale, kv->v_scale, layout, start_pos, B,
+                                    T, D, static_cast<hipStream_t>(stream));
+}
+
+size_t mqa_decode_paged_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,
+                                        int32_t block_size) {
+  if (check_decode_shape(B, Hq, D, max_seq_len) != MQA_OK) return 0;
+  if (block_size < 32 || block_size > 4096 || (block_size & (block_size - 1)) != 0) return 0;
+  return mqa::plan_decode(B, Hq, D, max_seq_len, window, device_cu_count(), block_size).ws_bytes;
+}
+
+namespace {
+int decode_paged_impl(const uint16_t* q, const mqa_kv_paged* kv, const float* k_new, const float* v_new,
+                      bool append, const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq,
+                      int32_t D, int32_t window, float softmax_scale, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_decode_common(q, seq_lens, out, B, Hq, D, max_seq_len);
+  if (st != MQA_OK) return st;
+  mqa::KVLayout layout;
+  st = check_paged(kv, &layout);
+  if (st != MQA_OK) return st;
+  if (append) {
+    if (!k_new || !v_new) return MQA_ERR_NULL;
+    if (((uintptr_t)k_new & 3u) || ((uintptr_t)v_new & 3u)) return MQA_ERR_ALIGN;
+  }
+  if (max_seq_len >= mqa::kPagedPositionLimit) return MQA_ERR_SHAPE;
+  if (!resident(kv, max_seq_len, window, window)) return MQA_ERR_SHAPE;
+  const mqa::DecodePlan plan =
+      mqa::plan_decode(B, Hq, D, max_seq_len, window, device_cu_count(), kv->block_size);
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+  }
+  const mqa_kv_view view{kv->k, kv->v, kv->k_scale, kv->v_scale, 0};
+  if (append) {
+    const mqa::AppendRows rows{k_new, v_new, kv->k, kv->v, kv->k_scale, kv->v_scale};
+    return mqa::launch_decode(q, view, layout, seq_lens, B, Hq, D, window, softmax_scale, out, workspace, plan,
+                              static_cast<hipStream_t>(stream), &rows);
+  }
+  return mqa::launch_decode(q, view, layout, seq_lens, B, Hq, D, window, softmax_scale, out, workspace, plan,
+                            static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+int mqa_decode_paged(const uint16_t* q, const mqa_kv_paged* kv, const int32_t* seq_lens, int32_t max_seq_len,
+                     int32_t B, int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_paged_impl(q, kv, nullptr, nullptr, false, seq_lens, max_seq_len, B, Hq, D, window,
+                           softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int mqa_decode_append_paged(const uint16_t* q, const mqa_kv_paged* kv, const float* k_new, const float* v_new,
+                            const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq, int32_t D,
+                            int32_t window, float softmax_scale, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_paged_impl(q, kv, k_new, v_new, true, seq_lens, max_seq_len, B, Hq, D, window, softmax_scale,
+                           out, workspace, workspace_bytes, stream);
+}
+
+int mqa_prefill_chunk_paged(const uint16_t* q, const mqa_kv_paged* kv, const int32_t* prefix_lens,
+                            int32_t max_prefix_len, int32_t B, int32_t C, int32_t Hq, int32_t D, int32_t window,
+                            float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!q || !prefix_lens || !out) return MQA_ERR_NULL;
+  mqa::KVLayout layout;
+  int st = check_paged(kv, &layout);
+  if (st != MQA_OK) return st;
+  if (B <= 0 || C <= 0 || Hq <= 0 || D <= 0 || max_prefix_len < 0) return MQA_ERR_SHAPE;
+  if (!supported_d(D) || !supported_hq(Hq)) return MQA_ERR_UNSUPPORTED;
+  if ((int64_t)max_prefix_len + C >= mqa::kPagedPositionLimit) return MQA_ERR_SHAPE;
+  if (!resident(kv, (int64_t)max_prefix_len + C, window, (int64_t)window + C - 1)) return MQA_ERR_SHAPE;
+  if ((int64_t)B > 65535) return MQA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(out)) return MQA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < mqa::prefill_workspace_bytes(B, C, D, max_prefix_len))
+    return MQA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+  const mqa_kv_view view{kv->k, kv->v, kv->k_scale, kv->v_scale, 0};
+  return mqa::launch_prefill(q, view, layout, prefix_lens, max_prefix_len, B, C, Hq, D, window, softmax_scale,
+                             out, workspace, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

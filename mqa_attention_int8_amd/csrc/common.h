@@ -213,6 +213,15 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t vo
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
+// Physical row of token position t of sequence b in a paged KV buffer:
+// block table[b][(t >> log2_bs) % table_len], entry clamped into the pool.
+__device__ __forceinline__ int64_t paged_row(const int32_t* table, int table_len, int log2_bs, int num_blocks,
+                                             int b, int t) {
+  int e = table[(int64_t)b * table_len + (t >> log2_bs) % table_len];
+  e = e < 0 ? 0 : (e >= num_blocks ? num_blocks - 1 : e);
+  return ((int64_t)e << log2_bs) | (t & ((1 << log2_bs) - 1));
+}
+
 // Streaming variants: the non-temporal hint (nt) for data read once per call.
 constexpr int kCachePolicyNT = 2;
 __device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {

@@ -70,6 +70,9 @@ constexpr int kHeadsPerGroup = 32;
 // Hence P'' < 2^(kLazy + 7) = 2^15 for every key, for any scales; the
 // accumulator is rescaled when either scale moves (rare).
 constexpr float kLazy = 8.0f;
+// Paged layout: block-table entries of one partition kept in LDS (the plan
+// bounds a partition's tiles so that they span fewer blocks).
+constexpr int kMaxTableSlice = 1024;
 constexpr int kValueHeadroom = 7;
 
 struct DecodeParams {
@@ -88,6 +91,13 @@ struct DecodeParams {
   int8_t* v_w;
   float* ks_w;
   float* vs_w;
+  // Paged layout (table != nullptr): k, v, ks, vs are block pools and token
+  // position t of sequence b is row table[b][(t >> log2_bs) % table_len]
+  // << log2_bs | (t & (2^log2_bs - 1)).
+  const int32_t* table;
+  int32_t table_len;
+  int32_t log2_bs;
+  int32_t num_blocks;
   float* ws_o;       // [B, P, Hq, D] partition outputs, normalised (natural d order)
   float2* ws_ml;     // [B, P, Hq] (offset m in log2 units, sum l of 2^(z - m))
   int32_t L_cap;
@@ -396,9 +406,9 @@ __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D /
 // Each wave keeps two tiles in registers: on entry `ta` holds the loads of its
 // tile ia and `tb` those of ib (> ia); a buffer is refilled with the next
 // handed-out tile as soon as it has been consumed.
-template <int D, int NT>
-__device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D, NT>& st, const SeqBuffers& sb,
-                                          const TileOffsets& off, const f16x8 (&qop)[NT][D / 32], float kscale,
+template <int D, int NT, typename Load>
+__device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D, NT>& st, const Load& load,
+                                          const f16x8 (&qop)[NT][D / 32], float kscale,
                                           int pt0, int count, int ia, int ib, int* next, int lane, int lo, int hi,
                                           int g, int new_tile, const float (&xk)[D / 64], const float (&xv)[D / 64],
                                           int8_t* scratch, bool write, int8_t* krow, int8_t* vrow, float* ks,
@@ -416,19 +426,20 @@ __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D,
       encode_new_row<D>(ta, xk, xv, scratch, hi - 1 - (pt0 + ia) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
     compute_tile<D, NT>(ta, st, qop, kscale, (pt0 + ia) * kTileKeys, lo, hi, g);
     ia = grab();
-    load_tile<D>(ta, sb, off, (pt0 + ia) * kTileKeys, ia < count);
+    load(ta, ia);
     if (ib >= count) break;
     if (ib == new_tile)
       encode_new_row<D>(tb, xk, xv, scratch, hi - 1 - (pt0 + ib) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
     compute_tile<D, NT>(tb, st, qop, kscale, (pt0 + ib) * kTileKeys, lo, hi, g);
     ib = grab();
-    load_tile<D>(tb, sb, off, (pt0 + ib) * kTileKeys, ib < count);
+    load(tb, ib);
   }
 }
 
 // WINDOWED: the layer attends to the last `window` keys (the partition's
 // tiles then depend on the sequence length); otherwise to all of them.
-template <int D, int NT, bool WINDOWED>
+// PAGED: the cache is a block pool addressed through p.table.
+template <int D, int NT, bool WINDOWED, bool PAGED>
 __global__ __launch_bounds__(64 * kWavesPerWG) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partition_kernel(DecodeParams p) {
   static_assert(NT == 1 || NT == 2, "a work-group serves at most 32 heads");
@@ -445,6 +456,7 @@ void decode_partition_kernel(DecodeParams p) {
   __shared__ float sm_l[WV][HP];
   __shared__ int sm_next;  // next tile (relative to pt0) to hand out
   __shared__ __attribute__((aligned(16))) int8_t sm_new[WV][2 * D];  // fused append: per-wave scratch
+  __shared__ int sm_tab[PAGED ? kMaxTableSlice : 1];  // physical blocks of the partition's tiles
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -458,13 +470,16 @@ void decode_partition_kernel(DecodeParams p) {
 
   const int tpp = p.tiles_per_part;
 
-  // One buffer resource per tensor of this sequence; loads past the cache
-  // capacity return zero (rows past the valid keys are masked anyway).
+  // Contiguous layout: one buffer resource per tensor of this sequence; loads
+  // past the cache capacity return zero (rows past the valid keys are masked
+  // anyway). Paged layout: resources are made per tile (below).
   SeqBuffers sb;
-  sb.k = make_rsrc(p.k + (int64_t)b * p.L_cap * D, (uint32_t)p.L_cap * D);
-  sb.v = make_rsrc(p.v + (int64_t)b * p.L_cap * D, (uint32_t)p.L_cap * D);
-  sb.ks = make_rsrc(p.ks + (int64_t)b * p.L_cap, (uint32_t)p.L_cap * 4);
-  sb.vs = make_rsrc(p.vs + (int64_t)b * p.L_cap, (uint32_t)p.L_cap * 4);
+  if (!PAGED) {
+    sb.k = make_rsrc(p.k + (int64_t)b * p.L_cap * D, (uint32_t)p.L_cap * D);
+    sb.v = make_rsrc(p.v + (int64_t)b * p.L_cap * D, (uint32_t)p.L_cap * D);
+    sb.ks = make_rsrc(p.ks + (int64_t)b * p.L_cap, (uint32_t)p.L_cap * 4);
+    sb.vs = make_rsrc(p.vs + (int64_t)b * p.L_cap, (uint32_t)p.L_cap * 4);
+  }
   TileOffsets off;
   off.k = (uint32_t)(c * D + g * (D / 4));
   off.v = (uint32_t)(4 * g * D + (D / 16) * c);
@@ -510,10 +525,10 @@ void decode_partition_kernel(DecodeParams p) {
   // tile this early too measured slower: the first work-groups' loads then
   // delay the q loads of those dispatched last.)
   Tile<D> ta, tb;
-  if (!WINDOWED) load_tile<D>(ta, sb, off, (part * tpp + wave) * kTileKeys, wave < tpp);
+  if (!WINDOWED && !PAGED) load_tile<D>(ta, sb, off, (part * tpp + wave) * kTileKeys, wave < tpp);
 
   int n = __builtin_amdgcn_readfirstlane(n_raw);  // same for the whole work-group
-  n = n < 0 ? 0 : (n > p.L_cap ? p.L_cap : n);
+  n = n < 0 ? 0 : (n > p.L_cap ? p.L_cap : n);     // paged: L_cap is the position bound
   const int lo = WINDOWED ? max(0, n - p.window) : 0;
   const int hi = n;
   const int t_begin = lo / kTileKeys;
@@ -523,9 +538,43 @@ void decode_partition_kernel(DecodeParams p) {
   const int count = pt1 - pt0;  // tiles of this partition (may be <= 0)
   // Fused append: the wave that draws the tile holding row n - 1 encodes it.
   const int new_tile = (appending && n > 0) ? (n - 1) / kTileKeys - pt0 : -1;  // outside [0, count): none here
-  const int64_t new_row = (int64_t)b * p.L_cap + (n > 0 ? n - 1 : 0);
-  if (WINDOWED) load_tile<D>(ta, sb, off, (pt0 + wave) * kTileKeys, wave < count);
-  load_tile<D>(tb, sb, off, (pt0 + wave + WV) * kTileKeys, wave + WV < count);
+
+  // Paged: the physical blocks of this partition's tiles, read once into LDS
+  // (entries clamped into the pool, so no access can leave it).
+  const int blk0 = PAGED ? (pt0 * kTileKeys) >> p.log2_bs : 0;
+  if (PAGED) {
+    const int nblk = count > 0 ? (((pt0 + count) * kTileKeys - 1) >> p.log2_bs) - blk0 + 1 : 0;
+    const int32_t* trow = p.table + (int64_t)b * p.table_len;
+    for (int i = threadIdx.x; i < nblk; i += NTHR) {
+      const int e = trow[(blk0 + i) % p.table_len];
+      sm_tab[i] = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);
+    }
+    __syncthreads();
+  }
+  // Physical row of token position `pos` (a position of this partition).
+  const auto phys_row = [&](int pos) -> int64_t {
+    if (!PAGED) return (int64_t)b * p.L_cap + pos;
+    const int e = sm_tab[(pos >> p.log2_bs) - blk0];
+    return ((int64_t)e << p.log2_bs) | (pos & ((1 << p.log2_bs) - 1));
+  };
+  const int64_t new_row = (new_tile >= 0 && new_tile < count) ? phys_row(n - 1) : 0;
+  // Loads of tile i of the partition (i >= count: nothing is read).
+  const auto load = [&](Tile<D>& t, int i) {
+    if (!PAGED) {
+      load_tile<D>(t, sb, off, (pt0 + i) * kTileKeys, i < count);
+    } else {
+      SeqBuffers tsb;
+      const int64_t row = i < count ? phys_row((pt0 + i) * kTileKeys) : 0;
+      const uint32_t kvb = i < count ? (uint32_t)(kTileKeys * D) : 0u, scb = i < count ? (uint32_t)(kTileKeys * 4) : 0u;
+      tsb.k = make_rsrc(p.k + row * D, kvb);
+      tsb.v = make_rsrc(p.v + row * D, kvb);
+      tsb.ks = make_rsrc(p.ks + row, scb);
+      tsb.vs = make_rsrc(p.vs + row, scb);
+      load_tile<D>(t, tsb, off, 0, i < count);
+    }
+  };
+  if (WINDOWED || PAGED) load(ta, wave);
+  load(tb, wave + WV);
 
   // Q^T as the B operand in fp16: the wave scales q by an exact power of two
   // that puts its largest |q| in [2^14, 2^15) and folds the scale into its
@@ -568,7 +617,7 @@ void decode_partition_kernel(DecodeParams p) {
   }
   st.vexp = -1000;
 
-  run_tiles<D, NT>(ta, tb, st, sb, off, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g,
+  run_tiles<D, NT>(ta, tb, st, load, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g,
                    new_tile, xk, xv, sm_new[wave], blockIdx.z == 0, p.k_w + new_row * D, p.v_w + new_row * D,
                    p.ks_w + new_row, p.vs_w + new_row);
 
@@ -691,22 +740,26 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   *reinterpret_cast<f32x4*>(out + ((int64_t)b * Hq + h) * D + d0) = acc * inv;
 }
 
-template <int D, int NT>
+template <int D, int NT, bool PAGED>
 void launch_partitions(const DecodeParams& prm, int B, hipStream_t stream) {
   const dim3 block(64 * kWavesPerWG);
   const dim3 grid(prm.num_parts, B, (prm.Hq + kHeadsPerGroup - 1) / kHeadsPerGroup);
   if (prm.window > 0)
-    hipLaunchKernelGGL((decode_partition_kernel<D, NT, true>), grid, block, 0, stream, prm);
+    hipLaunchKernelGGL((decode_partition_kernel<D, NT, true, PAGED>), grid, block, 0, stream, prm);
   else
-    hipLaunchKernelGGL((decode_partition_kernel<D, NT, false>), grid, block, 0, stream, prm);
+    hipLaunchKernelGGL((decode_partition_kernel<D, NT, false, PAGED>), grid, block, 0, stream, prm);
 }
 
 template <int D>
 void launch_by_heads(const DecodeParams& prm, int B, hipStream_t stream) {
-  if (prm.Hq <= 16)
-    launch_partitions<D, 1>(prm, B, stream);
-  else
-    launch_partitions<D, 2>(prm, B, stream);
+  const bool paged = prm.table != nullptr;
+  if (prm.Hq <= 16) {
+    if (paged) launch_partitions<D, 1, true>(prm, B, stream);
+    else launch_partitions<D, 1, false>(prm, B, stream);
+  } else {
+    if (paged) launch_partitions<D, 2, true>(prm, B, stream);
+    else launch_partitions<D, 2, false>(prm, B, stream);
+  }
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -715,7 +768,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 }  // namespace
 
 DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,
-                       int num_cus) {
+                       int num_cus, int32_t block_size) {
   DecodePlan pl{1, 1, 0};
   // Upper bound of 32-key tiles a sequence's visible range can touch.
   int64_t ntiles;
@@ -731,6 +784,11 @@ DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, in
   int64_t tpp = ((int64_t)B * groups * ntiles + target - 1) / target;
   if (tpp < wv) tpp = wv;
   if (tpp > ntiles) tpp = ntiles;
+  // Paged: a partition's tiles must span at most kMaxTableSlice blocks.
+  if (block_size > 0) {
+    const int64_t cap = (int64_t)(kMaxTableSlice - 2) * block_size / kTileKeys;
+    if (tpp > cap) tpp = cap;
+  }
   const int64_t parts = (ntiles + tpp - 1) / tpp;
   pl.tiles_per_part = (int)tpp;
   pl.num_parts = (int)parts;
@@ -741,10 +799,14 @@ DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, in
   return pl;
 }
 
-int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const int32_t* seq_lens, int32_t B,
-                  int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
+int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layout, const int32_t* seq_lens,
+                  int32_t B, int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
                   void* workspace, const DecodePlan& plan, hipStream_t stream, const AppendRows* append) {
   DecodeParams prm;
+  prm.table = layout.table;
+  prm.table_len = layout.table_len;
+  prm.log2_bs = layout.log2_bs;
+  prm.num_blocks = layout.num_blocks;
   prm.k_new = append ? append->k_new : nullptr;
   prm.v_new = append ? append->v_new : nullptr;
   prm.k_w = append ? append->k : nullptr;
@@ -758,7 +820,7 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const int32_t* seq_l
   prm.vs = kv.v_scale;
   prm.seq_lens = seq_lens;
   prm.out = out;
-  prm.L_cap = kv.L_cap;
+  prm.L_cap = layout.table ? layout.L_cap : kv.L_cap;
   prm.Hq = Hq;
   prm.window = window;
   prm.tiles_per_part = plan.tiles_per_part;

@@ -9,17 +9,36 @@
 
 namespace mqa {
 
+// Where the token rows of a KV buffer live. Contiguous (table == nullptr):
+// row b * L_cap + t. Paged: row table[b][(t >> log2_bs) % table_len] <<
+// log2_bs | (t mod 2^log2_bs), with entries clamped into [0, num_blocks);
+// L_cap then bounds token positions.
+struct KVLayout {
+  const int32_t* table = nullptr;
+  int32_t table_len = 0;
+  int32_t log2_bs = 0;
+  int32_t num_blocks = 0;
+  int32_t L_cap = 0;
+};
+// Position bound of a paged buffer (positions wrap around a short table).
+constexpr int32_t kPagedPositionLimit = 1 << 30;
+
 // Sequence-partition plan of one decode call (host side, pure function).
 struct DecodePlan {
   int tiles_per_part;  // 32-key tiles per work-group
   int num_parts;       // work-groups per sequence
   size_t ws_bytes;     // workspace for partial states (0 when num_parts == 1)
 };
+// block_size > 0: paged layout (bounds the tiles of a partition).
 DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,
-                       int num_cus);
+                       int num_cus, int32_t block_size = 0);
 
 int launch_quantize(const float* src, int8_t* dst, float* dst_scale, const int32_t* start_pos,
                     int32_t B, int32_t T, int32_t D, int32_t L_cap, hipStream_t stream);
+// K and V rows of T new tokens per sequence into a paged buffer (one launch).
+int launch_quantize_paged(const float* k_src, const float* v_src, int8_t* k, int8_t* v, float* k_scale,
+                          float* v_scale, const KVLayout& layout, const int32_t* start_pos, int32_t B,
+                          int32_t T, int32_t D, hipStream_t stream);
 
 // Fused append of one new token per sequence (writable view of the cache the
 // attention reads, and the new fp32 rows).
@@ -32,16 +51,16 @@ struct AppendRows {
   float* v_scale;
 };
 
-int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const int32_t* seq_lens, int32_t B,
-                  int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
+int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layout, const int32_t* seq_lens,
+                  int32_t B, int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
                   void* workspace, const DecodePlan& plan, hipStream_t stream,
                   const AppendRows* append = nullptr);
 
 size_t prefill_workspace_bytes(int32_t B, int32_t C, int32_t D, int32_t max_prefix_len);
 
-int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const int32_t* prefix_lens,
-                   int32_t max_prefix_len, int32_t B, int32_t C, int32_t Hq, int32_t D,
-                   int32_t window, float softmax_scale, float* out, void* workspace,
+int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layout,
+                   const int32_t* prefix_lens, int32_t max_prefix_len, int32_t B, int32_t C, int32_t Hq,
+                   int32_t D, int32_t window, float softmax_scale, float* out, void* workspace,
                    hipStream_t stream);
 
 }  // namespace mqa

@@ -72,17 +72,29 @@ struct PrefillParams {
   float* out;
   char* stage;          // [B][ntiles][StagedTile]
   float* seq_e;         // [B] exponent E of each sequence (as float)
-  int32_t L_cap;
+  int32_t L_cap;         // contiguous: rows per sequence; paged: position bound
+  // Paged layout (table != nullptr): k, v, ks, vs are block pools.
+  const int32_t* table;
+  int32_t table_len;
+  int32_t log2_bs;
+  int32_t num_blocks;
   int32_t C;
   int32_t Hq;
   int32_t window;
   int32_t ntiles;       // tiles per sequence in the workspace
+  int32_t P_max;        // prefix lengths are clamped to [0, P_max] (workspace and cache bounds)
   int32_t row_tiles;    // attention work-groups per sequence
   float scale_log2;
 };
 
-__device__ __forceinline__ int clampP(int P, int L_cap, int C) {
-  return P < 0 ? 0 : (P > L_cap - C ? L_cap - C : P);
+// Physical row of key position j of sequence b.
+__device__ __forceinline__ int64_t key_row(const PrefillParams& p, int b, int j) {
+  if (p.table == nullptr) return (int64_t)b * p.L_cap + j;
+  return paged_row(p.table, p.table_len, p.log2_bs, p.num_blocks, b, j);
+}
+
+__device__ __forceinline__ int clampP(int P, int P_max) {
+  return P < 0 ? 0 : (P > P_max ? P_max : P);
 }
 
 __device__ __forceinline__ int first_needed_key(int P, int window) {
@@ -96,11 +108,10 @@ __device__ __forceinline__ int first_needed_key(int P, int window) {
 __global__ __launch_bounds__(256) void prefill_exponent_kernel(PrefillParams p) {
   const int b = blockIdx.x, tid = threadIdx.x;
   __shared__ float red[4];
-  const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.L_cap, p.C);
+  const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.P_max);
   const int lo = first_needed_key(P, p.window), hi = P + p.C;
-  const float* vs = p.vs + (int64_t)b * p.L_cap;
   float m = 0.f;
-  for (int j = lo + tid; j < hi; j += 256) m = fmaxf(m, fabsf(vs[j]));
+  for (int j = lo + tid; j < hi; j += 256) m = fmaxf(m, fabsf(p.vs[key_row(p, b, j)]));
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, kWave));
   if ((tid & 63) == 0) red[tid >> 6] = m;
@@ -119,15 +130,13 @@ __global__ __launch_bounds__(256) void prefill_exponent_kernel(PrefillParams p) 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
   const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.L_cap, p.C);
+  const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.P_max);
   const int kend = P + p.C;                            // keys [0, kend) exist
   const int t_lo = first_needed_key(P, p.window) / kKeys;
   const int t_hi = (kend + kKeys - 1) / kKeys;
   if (t < t_lo || t >= t_hi) return;
   const int base = t * kKeys;
   char* tile = p.stage + ((int64_t)b * p.ntiles + t) * StagedTile<D>::kBytes;
-  const int8_t* kb = p.k + (int64_t)b * p.L_cap * D;
-  const int8_t* vb = p.v + (int64_t)b * p.L_cap * D;
 
   // K: thread = (key, quarter of the row); 16-byte chunk c of row `key` is
   // stored at chunk c ^ (key & 7).
@@ -138,7 +147,7 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
     u32x4 w[QB / 16];
 #pragma unroll
     for (int u = 0; u < QB / 16; ++u)
-      w[u] = j < kend ? *reinterpret_cast<const u32x4*>(kb + (int64_t)j * D + qtr * QB + 16 * u)
+      w[u] = j < kend ? *reinterpret_cast<const u32x4*>(p.k + key_row(p, b, j) * D + qtr * QB + 16 * u)
                       : u32x4{0u, 0u, 0u, 0u};
     uint16_t* row = reinterpret_cast<uint16_t*>(tile) + key * D;
 #pragma unroll
@@ -156,7 +165,6 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
   {
     constexpr int DQ = D / 4;   // 4-column groups
     const float rE = exp2f(-p.seq_e[b]);
-    const float* vsb = p.vs + (int64_t)b * p.L_cap;
     for (int it = tid; it < 8 * DQ; it += 256) {
       const int grp = it / DQ, dq = it % DQ;
       const int ks = grp >> 2, g = grp & 3;
@@ -166,8 +174,9 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
       for (int i = 0; i < 8; ++i) {
         const int j = base + 32 * ks + 16 * (i >> 2) + 4 * g + (i & 3);
         const bool ok = j < kend;
-        w[i] = ok ? *reinterpret_cast<const uint32_t*>(vb + (int64_t)j * D + 4 * dq) : 0u;
-        f[i] = ok ? vsb[j] * rE : 0.f;   // exact: a power-of-two rescale
+        const int64_t row = ok ? key_row(p, b, j) : 0;
+        w[i] = ok ? *reinterpret_cast<const uint32_t*>(p.v + row * D + 4 * dq) : 0u;
+        f[i] = ok ? p.vs[row] * rE : 0.f;   // exact: a power-of-two rescale
       }
       uint16_t* vt = reinterpret_cast<uint16_t*>(tile + StagedTile<D>::kBytesK);
 #pragma unroll
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
   // Per-key s_k * scale * log2(e).
   if (tid < kKeys) {
     const int j = base + tid;
-    const float sk = j < kend ? p.ks[(int64_t)b * p.L_cap + j] * p.scale_log2 : 0.f;
+    const float sk = j < kend ? p.ks[key_row(p, b, j)] * p.scale_log2 : 0.f;
     reinterpret_cast<float*>(tile + StagedTile<D>::kOffScl)[tid] = sk;
   }
 }
@@ -327,7 +336,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
   const int C = p.C, Hq = p.Hq;
   const int rows_total = C * Hq;
-  const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.L_cap, C);
+  const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.P_max);
 
   const int wg_r0 = mtile * kRowsPerWG;
   const int wg_r1 = min(wg_r0 + kRowsPerWG, rows_total);
@@ -428,7 +437,7 @@ size_t prefill_workspace_bytes(int32_t B, int32_t C, int32_t D, int32_t max_pref
   return stage + expo;
 }
 
-int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const int32_t* prefix_lens,
+int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layout, const int32_t* prefix_lens,
                    int32_t max_prefix_len, int32_t B, int32_t C, int32_t Hq, int32_t D,
                    int32_t window, float softmax_scale, float* out, void* workspace,
                    hipStream_t stream) {
@@ -440,12 +449,19 @@ int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const int32_t* pref
   prm.vs = kv.v_scale;
   prm.prefix_lens = prefix_lens;
   prm.out = out;
-  prm.L_cap = kv.L_cap;
+  prm.L_cap = layout.table ? layout.L_cap : kv.L_cap;
+  prm.table = layout.table;
+  prm.table_len = layout.table_len;
+  prm.log2_bs = layout.log2_bs;
+  prm.num_blocks = layout.num_blocks;
   prm.C = C;
   prm.Hq = Hq;
   prm.window = window;
   prm.scale_log2 = softmax_scale * 1.4426950408889634f;
   prm.ntiles = (int)(((int64_t)max_prefix_len + C + kKeys - 1) / kKeys);
+  // A prefix longer than max_prefix_len would reach past this sequence's
+  // staged tiles; one past the cache capacity past the cache.
+  prm.P_max = (int)((int64_t)max_prefix_len < (int64_t)prm.L_cap - C ? max_prefix_len : prm.L_cap - C);
   const size_t tb = (D == 128) ? StagedTile<128>::kBytes : StagedTile<64>::kBytes;
   prm.stage = static_cast<char*>(workspace);
   prm.seq_e = reinterpret_cast<float*>(prm.stage + (size_t)B * prm.ntiles * tb);

@@ -5,4 +5,5 @@ from .mqa_oracle import (quantize_rows, dequantize_rows, bf16_bits_to_f64,
                          attend, attention_weights, decode_ref, decode_ref_rows,
                          prefill_ref, lse_partial, lse_merge, hybrid_block_ref,
                          kv_bytes_per_token, int8_kv_bytes_per_key,
-                         decode_visible_keys, prefill_visible_pairs)
+                         decode_visible_keys, prefill_visible_pairs,
+                         paged_rows, paged_gather, paged_scatter, paged_window_resident)

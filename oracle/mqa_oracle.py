@@ -28,6 +28,13 @@ What it computes, and where that comes from:
   energy = q.k, softmax of the scaled energy over keys, weighted sum of
   values; the scale there divides by the square root of the model width,
   here it is an explicit argument defaulting to 1/sqrt(head_dim).]
+* Paged KV buffers: a sequence's KV is logically contiguous but stored in
+  fixed-size blocks of a shared pool, mapped through a per-sequence table
+  and allocated as tokens arrive.  [workshop transcript, 01:01:35-01:03:22
+  (PagedAttention).]  A table shorter than the sequence wraps around, so a
+  window-only buffer keeps just the recent blocks [9c1h.cn page, "秘訣1",
+  item "混合注意力視野": local layers need only the last 1024 tokens];
+  ``paged_rows`` / ``paged_gather`` / ``paged_scatter`` write the mapping out.
 * The online-softmax / partition merge is an exact rewrite of softmax
   [workshop transcript, 00:48:02-00:49:13: tiles kept in fast memory with
   three running quantities for an online softmax]; ``lse_merge`` writes the
@@ -315,3 +322,48 @@ def prefill_visible_pairs(prefix_lens, chunk, window):
             lo, hi = prefill_visible(int(P) + i, window)
             tot += hi - lo
     return tot
+
+
+# ---------------------------------------------------------------------------
+# Paged KV buffers  [workshop transcript 01:01:35-01:03:22 (logical blocks of
+# a sequence mapped to physical blocks of a pool); 9c1h.cn "秘訣1" (a local
+# layer only needs its window, so its blocks can be reused as a ring)]
+# ---------------------------------------------------------------------------
+
+
+def paged_rows(table: np.ndarray, block_size: int, b: int, positions) -> np.ndarray:
+    """Pool rows of token positions of sequence ``b``: the logical block of a
+    position is position // block_size; the table (row b, wrapping around its
+    length) names the pool block; the offset inside the block is kept."""
+    t = np.asarray(positions, dtype=np.int64)
+    logical_block = t // block_size
+    pool_block = np.asarray(table, dtype=np.int64)[b, logical_block % table.shape[1]]
+    return pool_block * block_size + t % block_size
+
+
+def paged_gather(pool: np.ndarray, table: np.ndarray, block_size: int, L: int) -> np.ndarray:
+    """Logical view [B, L, ...] of a pool [num_blocks, block_size, ...]."""
+    flat = pool.reshape((pool.shape[0] * block_size,) + pool.shape[2:])
+    B = table.shape[0]
+    return np.stack([flat[paged_rows(table, block_size, b, np.arange(L))] for b in range(B)])
+
+
+def paged_scatter(pool: np.ndarray, table: np.ndarray, block_size: int, rows: np.ndarray,
+                  start_pos) -> None:
+    """Write rows[b, i] (in order of i) at position start_pos[b] + i of sequence b."""
+    flat = pool.reshape((pool.shape[0] * block_size,) + pool.shape[2:])
+    for b in range(rows.shape[0]):
+        for i in range(rows.shape[1]):
+            pos = int(start_pos[b]) + i
+            if pos < 0:
+                continue
+            flat[paged_rows(table, block_size, b, [pos])[0]] = rows[b, i]
+
+
+def paged_window_resident(window: int, table_len: int, block_size: int) -> bool:
+    """Whether a wrapping table still holds the last ``window`` positions
+    after positions are appended in order: position t and t + table_len *
+    block_size share a pool row, so exactly the last table_len * block_size
+    positions are kept."""
+    return window <= table_len * block_size
+

@@ -99,3 +99,12 @@ def kv_rows_f32(wid: int, which: int, buffer_id: int, B: int, L: int, D: int) ->
     """fp32 N(0,1) K (which=T_K) or V (which=T_V) rows of one buffer, [B, L, D]."""
     g = rng(wid, which, buffer_id)
     return normal_f32(g, (B, L, D))
+
+
+def block_table(g: np.random.Generator, B: int, table_len: int, num_blocks: int) -> np.ndarray:
+    """int32 [B, table_len]: distinct pool blocks drawn at random (a shuffled
+    allocation, as a block allocator under churn would leave it)."""
+    if B * table_len > num_blocks:
+        raise ValueError("pool too small for distinct blocks")
+    return g.permutation(num_blocks)[: B * table_len].reshape(B, table_len).astype(np.int32)
+

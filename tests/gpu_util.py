@@ -89,3 +89,25 @@ def assert_prefill_close(gpu: torch.Tensor, ref: np.ndarray, atol=5e-3, rtol=1e-
     log(f"  {what}: max |gpu - oracle| = {err:.3e}, worst margin {float(excess.max()):.3e}")
     assert np.all(excess <= 0), f"{what}: {int((excess > 0).sum())} elements outside atol+rtol*|ref|"
     return err
+
+
+def block_copy_pool(cont: np.ndarray, table: np.ndarray, bs: int, num_blocks: int, fill=0) -> np.ndarray:
+    """Pool [num_blocks, bs, ...] built from a contiguous cache [B, L, ...] by
+    whole-block copies: logical block j of sequence b -> pool block table[b, j]
+    (blocks past L // bs are left at ``fill``)."""
+    B, L = cont.shape[:2]
+    pool = np.full((num_blocks, bs) + cont.shape[2:], fill, cont.dtype)
+    for b in range(B):
+        for j in range(min(L // bs, table.shape[1])):
+            pool[table[b, j]] = cont[b, j * bs:(j + 1) * bs]
+    return pool
+
+
+def paged_from_host(hkv: "HostKV", table: np.ndarray, bs: int, num_blocks: int):
+    """PagedKV on the device holding the same rows as a host cache."""
+    from mqa_attention_int8_amd import PagedKV
+    kq, ks, vq, vs = hkv.arrays()
+    return PagedKV(dev(block_copy_pool(kq, table, bs, num_blocks)), dev(block_copy_pool(vq, table, bs, num_blocks)),
+                   dev(block_copy_pool(ks, table, bs, num_blocks)), dev(block_copy_pool(vs, table, bs, num_blocks)),
+                   dev(np.ascontiguousarray(table, dtype=np.int32)))
+

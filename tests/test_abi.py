@@ -26,7 +26,8 @@ def declared_functions():
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert {"kv_quantize_int8", "mqa_decode", "mqa_decode_append", "mqa_prefill_chunk",
-            "mqa_decode_workspace_bytes", "mqa_status_string"} <= set(names)
+            "mqa_decode_workspace_bytes", "mqa_status_string", "kv_quantize_int8_paged", "mqa_decode_paged",
+            "mqa_decode_append_paged", "mqa_prefill_chunk_paged", "mqa_decode_paged_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in mqa_int8.h but not exported"
 
@@ -151,3 +152,72 @@ def test_decode_append_validation(lib):
     assert append(lib, kv=mqa_kv_cache(FAKE, FAKE, FAKE, FAKE, 62), max_len=60) == 4   # scales 4 at a time
     # many partitions need a workspace
     assert append(lib, B=8, max_len=60000, kv=mqa_kv_cache(FAKE, FAKE, FAKE, FAKE, 65536)) == 5
+
+
+def paged(bs=32, TL=8, nb=64, table=FAKE, k=FAKE, ks=FAKE):
+    from mqa_attention_int8_amd.binding import mqa_kv_paged
+    return mqa_kv_paged(k, FAKE, ks, FAKE, table, bs, TL, nb)
+
+
+def decode_paged(lib, **kw):
+    a = dict(q=FAKE, kv=paged(), seq=FAKE, max_len=64, B=2, Hq=8, D=128, W=0, scale=0.1, out=FAKE,
+             ws=None, ws_bytes=0)
+    a.update(kw)
+    v = a["kv"]
+    return lib.mqa_decode_paged(a["q"], ctypes.byref(v) if v is not None else None, a["seq"], a["max_len"],
+                                a["B"], a["Hq"], a["D"], a["W"], a["scale"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_paged_validation(lib):
+    NULL, SHAPE, UNSUP, ALIGN = 1, 2, 3, 4
+    assert decode_paged(lib, kv=None) == NULL
+    assert decode_paged(lib, kv=paged(table=None)) == NULL
+    for bs in (16, 48, 8192, 0):
+        assert decode_paged(lib, kv=paged(bs=bs)) == SHAPE, bs
+    assert decode_paged(lib, kv=paged(TL=0)) == SHAPE
+    assert decode_paged(lib, kv=paged(nb=0)) == SHAPE
+    assert decode_paged(lib, kv=paged(k=FAKE + 8)) == ALIGN
+    assert decode_paged(lib, kv=paged(ks=FAKE + 4)) == ALIGN
+    assert decode_paged(lib, kv=paged(table=FAKE + 2)) == ALIGN
+    assert decode_paged(lib, D=96) == UNSUP
+    # the table (8 blocks of 32 = 256 positions) wraps for longer sequences:
+    # only a windowed layer whose window fits in those 256 positions may read it
+    assert decode_paged(lib, max_len=257, W=0) == SHAPE
+    assert decode_paged(lib, max_len=4096, W=257) == SHAPE
+    # a window that fits passes validation and then needs its workspace
+    assert lib.mqa_decode_paged_workspace_bytes(2, 8, 128, 4096, 256, 32) > 0
+    assert decode_paged(lib, max_len=4096, W=256, ws=None, ws_bytes=0) == 5
+    assert lib.mqa_decode_paged_workspace_bytes(2, 8, 128, 4096, 0, 48) == 0
+
+
+def test_decode_append_paged_validation(lib):
+    kvp = paged()
+    r = lib.mqa_decode_append_paged(FAKE, ctypes.byref(kvp), None, FAKE, FAKE, 64, 2, 8, 128, 0, 0.1, FAKE, None,
+                                    0, None)
+    assert r == 1
+    r = lib.mqa_decode_append_paged(FAKE, ctypes.byref(kvp), FAKE + 2, FAKE, FAKE, 64, 2, 8, 128, 0, 0.1, FAKE,
+                                    None, 0, None)
+    assert r == 4
+
+
+def test_quantize_paged_validation(lib):
+    kvp = paged()
+    q = lambda **kw: lib.kv_quantize_int8_paged(kw.get("k", FAKE), FAKE, ctypes.byref(kw.get("kv", kvp)), FAKE,
+                                                kw.get("B", 2), kw.get("T", 4), kw.get("D", 128), None)
+    assert q(k=None) == 1
+    assert q(T=0) == 2
+    assert q(T=257) == 2      # one call would write a pool row twice
+    assert q(D=32) == 3
+    assert q(k=FAKE + 4) == 4
+    assert q(kv=paged(bs=100)) == 2
+
+
+def test_prefill_paged_validation(lib):
+    def pf(kvp, max_prefix=64, C=16, W=0, ws=FAKE, ws_bytes=1 << 40):
+        return lib.mqa_prefill_chunk_paged(FAKE, ctypes.byref(kvp), FAKE, max_prefix, 2, C, 8, 128, W, 0.1, FAKE,
+                                           ws, ws_bytes, None)
+    assert pf(paged(table=None)) == 1
+    assert pf(paged(), max_prefix=250, C=16, W=0) == 2          # global layer past the table
+    assert pf(paged(), max_prefix=1000, C=16, W=242) == 2       # W + C - 1 = 257 > 256
+    assert pf(paged(), max_prefix=64, C=16, ws=None, ws_bytes=0) == 5
+
