@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the hybrid/long/prefill lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
-    ap.add_argument("--only", choices=["decode", "hybrid", "long", "prefill"], default=None,
+    ap.add_argument("--only", choices=["decode", "hybrid", "long", "prefill", "paged"], default=None,
                     help="time a single workload (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -232,6 +232,86 @@ def bench_long(torch, m, acct, stream):
             "frac_hbm_peak": kv / (ms_call * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
+def bench_paged(torch, m, acct, stream):
+    """Paged layouts on the decode workload's shape: the global layer (fused
+    append) over a pool of 32-token blocks in shuffled order, and a window-1024
+    layer over a ring of 1024 slots per sequence; each against the same call on
+    contiguous buffers, timed in this run."""
+    B, Hq, D, L, bs, W = 64, 32, 128, 4096, 32, 1024
+    TL = L // bs
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    per = B * L * (2 * D + 8)
+    R = max(2, math.ceil((1 << 30) / per))
+    cont = make_decode_buffers(torch, m, B, L, D, R, gen)
+    pools = []
+    for kv in cont:
+        perm = torch.randperm(B * TL, generator=gen, device="cuda")
+        table = perm.view(B, TL).to(torch.int32).contiguous()
+        pk = torch.empty((B * TL, bs, D), dtype=torch.int8, device="cuda")
+        pv = torch.empty_like(pk)
+        pks = torch.empty((B * TL, bs), dtype=torch.float32, device="cuda")
+        pvs = torch.empty_like(pks)
+        pk[perm] = kv.k.view(B * TL, bs, D)
+        pv[perm] = kv.v.view(B * TL, bs, D)
+        pks[perm] = kv.k_scale.view(B * TL, bs)
+        pvs[perm] = kv.v_scale.view(B * TL, bs)
+        pools.append(m.PagedKV(pk, pv, pks, pvs, table))
+    # window-only ring buffers: 1024 slots per sequence, positions 0..L-1 appended in order
+    TLr = W // bs
+    ring_per = B * W * (2 * D + 8)
+    Rr = max(2, math.ceil((1 << 30) / ring_per))
+    rings = []
+    for _ in range(Rr):
+        table = torch.randperm(B * TLr, generator=gen, device="cuda").view(B, TLr).to(torch.int32).contiguous()
+        kvr = m.PagedKV.empty(B * TLr, bs, D, table)
+        kvr.k.copy_(torch.randint(-127, 128, kvr.k.shape, generator=gen, device="cuda", dtype=torch.int8))
+        kvr.v.copy_(torch.randint(-127, 128, kvr.v.shape, generator=gen, device="cuda", dtype=torch.int8))
+        kvr.k_scale.copy_(torch.rand(kvr.k_scale.shape, generator=gen, device="cuda") * 0.03)
+        kvr.v_scale.copy_(torch.rand(kvr.v_scale.shape, generator=gen, device="cuda") * 0.03)
+        rings.append(kvr)
+    seq_lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    q = torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    knew = torch.randn((B, D), generator=gen, device="cuda")
+    vnew = torch.randn((B, D), generator=gen, device="cuda")
+    out = torch.empty((B, Hq, D), device="cuda")
+    ws_c = [m.decode_workspace(B, Hq, D, L, w) for w in (0, W)]
+    nws = max(m.mqa_decode_paged_workspace_bytes(B, Hq, D, L, w, bs) for w in (0, W))
+    ws_p = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+
+    def g_cont():
+        for kv in cont:
+            m.mqa_decode_append(q, kv, knew, vnew, seq_lens, L, 0, out=out, workspace=ws_c[0])
+
+    def g_paged():
+        for kv in pools:
+            m.mqa_decode_append_paged(q, kv, knew, vnew, seq_lens, L, 0, out=out, workspace=ws_p)
+
+    def w_cont():
+        for kv in cont:
+            m.mqa_decode(q, kv, seq_lens, L, W, out=out, workspace=ws_c[1])
+
+    def w_ring():
+        for kv in rings:
+            m.mqa_decode_paged(q, kv, seq_lens, L, W, out=out, workspace=ws_p)
+
+    res = {"workload": "decode_B64_Hq32_D128_L4096", "block_size": bs, "ring_slots": W}
+    with torch.cuda.stream(stream):
+        for name, fn, n in (("global_contiguous_us", g_cont, R), ("global_paged_us", g_paged, R),
+                            ("window_contiguous_us", w_cont, R), ("window_ring_us", w_ring, Rr)):
+            fn()
+            torch.cuda.synchronize()
+            reps = 20
+            ms, _ = run_steps(torch, fn, reps, True, stream)
+            res[name] = ms * 1e3 / (reps * n)
+    kv_g = acct.decode_kv_bytes([L] * B, 0, D)
+    kv_w = acct.decode_kv_bytes([L] * B, W, D)
+    res["global_paged_GBps"] = kv_g / (res["global_paged_us"] * 1e-6) / 1e9
+    res["window_ring_GBps"] = kv_w / (res["window_ring_us"] * 1e-6) / 1e9
+    res["window_buffer_bytes_per_seq"] = {"ring": W * (2 * D + 8), "contiguous": L * (2 * D + 8)}
+    return res
+
+
 def bench_prefill(torch, m, acct, stream):
     B, C, P, Hq, D = 16, 512, 8192, 32, 128
     gen = torch.Generator(device="cuda")
@@ -346,6 +426,8 @@ def main():
             extra["long_context"] = bench_long(torch, m, acct, stream)
         if args.only in (None, "prefill"):
             extra["prefill"] = bench_prefill(torch, m, acct, stream)
+        if args.only in (None, "paged"):
+            extra["paged"] = bench_paged(torch, m, acct, stream)
     if dec is None:
         print(json.dumps({"extra": extra}))
         return
