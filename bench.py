@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the hybrid/long/prefill lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
-    ap.add_argument("--only", choices=["decode", "hybrid", "long", "prefill", "paged"], default=None,
+    ap.add_argument("--only", choices=["decode", "hybrid", "long", "prefill", "paged", "q8"], default=None,
                     help="time a single workload (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -312,6 +312,57 @@ def bench_paged(torch, m, acct, stream):
     return res
 
 
+def bench_q8(torch, m, acct, stream):
+    """The decode step of the main workload with int8 queries (int8 MFMA for
+    Q K^T; the query rows encoded by kv_quantize_int8 outside the timed
+    region, as a projection with int8 outputs would deliver them), against the
+    bf16-query step in the same run."""
+    B, Hq, D, L = 64, 32, 128, 4096
+    windows = (0, 1024)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8)
+    R = max(2, math.ceil((1 << 30) / (B * L * (2 * D + 8))))
+    bufs = make_decode_buffers(torch, m, B, L, D, R, gen)
+    seq_lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    qf = [torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in windows]
+    q8 = [torch.empty((B, Hq, D), dtype=torch.int8, device="cuda") for _ in windows]
+    qs = [torch.empty((B, Hq), dtype=torch.float32, device="cuda") for _ in windows]
+    for i in range(len(windows)):
+        m.kv_quantize_int8(qf[i].float().contiguous(), q8[i], qs[i], zero)
+    knew = torch.randn((B, D), generator=gen, device="cuda")
+    vnew = torch.randn((B, D), generator=gen, device="cuda")
+    out = torch.empty((B, Hq, D), device="cuda")
+    ws = [m.decode_workspace(B, Hq, D, L, w) for w in windows]
+
+    def step_bf16():
+        for kv in bufs:
+            m.mqa_decode_append(qf[0], kv, knew, vnew, seq_lens, L, 0, out=out, workspace=ws[0])
+            m.mqa_decode(qf[1], kv, seq_lens, L, windows[1], out=out, workspace=ws[1])
+
+    def step_q8():
+        for kv in bufs:
+            m.mqa_decode_append_q8(q8[0], qs[0], kv, knew, vnew, seq_lens, L, 0, out=out, workspace=ws[0])
+            m.mqa_decode_q8(q8[1], qs[1], kv, seq_lens, L, windows[1], out=out, workspace=ws[1])
+
+    def global_q8():
+        for kv in bufs:
+            m.mqa_decode_append_q8(q8[0], qs[0], kv, knew, vnew, seq_lens, L, 0, out=out, workspace=ws[0])
+
+    res = {"workload": "decode_B64_Hq32_D128_L4096 (global + window-1024 layer), int8 queries"}
+    with torch.cuda.stream(stream):
+        for name, fn in (("step_bf16_us", step_bf16), ("step_q8_us", step_q8), ("global_q8_us", global_q8)):
+            fn()
+            torch.cuda.synchronize()
+            reps = 20
+            ms, _ = run_steps(torch, fn, reps, True, stream)
+            res[name] = ms * 1e3 / (reps * R)
+    res["tokens_per_s_q8"] = B / (res["step_q8_us"] * 1e-6)
+    kv_g = acct.decode_kv_bytes([L] * B, 0, D)
+    res["global_q8_GBps"] = kv_g / (res["global_q8_us"] * 1e-6) / 1e9
+    return res
+
+
 def bench_prefill(torch, m, acct, stream):
     B, C, P, Hq, D = 16, 512, 8192, 32, 128
     gen = torch.Generator(device="cuda")
@@ -428,6 +479,8 @@ def main():
             extra["prefill"] = bench_prefill(torch, m, acct, stream)
         if args.only in (None, "paged"):
             extra["paged"] = bench_paged(torch, m, acct, stream)
+        if args.only in (None, "q8"):
+            extra["q8"] = bench_q8(torch, m, acct, stream)
     if dec is None:
         print(json.dumps({"extra": extra}))
         return

@@ -269,6 +269,38 @@ int mqa_prefill_chunk_paged(const uint16_t* q, const mqa_kv_paged* kv,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* ---------------------------------------------------------------------------
+ * int8 queries. [explinks.com page "Character.AI 的最佳实践", sections
+ * "训练和服务的量化" (weights, activations and the KV cache all in int8) and
+ * "int8 内核实现" (custom int8 kernels for matmuls and attention).] The
+ * query of each (token, head) row is int8 with one fp32 scale, encoded like
+ * a KV row (kv_quantize_int8 applied to the fp32 queries viewed as
+ * [B, Hq, D] rows produces exactly this input). Q K^T then runs on int8
+ * matrix cores: logit_j = softmax_scale * q_scale * k_scale[j] * (q8 . k8_j)
+ * with the integer dot product exact; the rest is as in mqa_decode. This
+ * changes the numerics (the query carries 8 bits instead of bf16's): results
+ * match the same attention computed with the int8 queries, not mqa_decode's.
+ * ------------------------------------------------------------------------- */
+
+/* mqa_decode_q8 - mqa_decode with int8 queries.
+ *   q8       int8 [B, Hq, D] (16-byte aligned); q_scale fp32 [B, Hq]
+ *            (4-byte aligned). Other arguments, workspace
+ *            (mqa_decode_workspace_bytes) and errors as mqa_decode. */
+int mqa_decode_q8(const int8_t* q8, const float* q_scale, const mqa_kv_view* kv,
+                  const int32_t* seq_lens, int32_t max_seq_len, int32_t B,
+                  int32_t Hq, int32_t D, int32_t window, float softmax_scale,
+                  float* out, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* mqa_decode_append_q8 - mqa_decode_append with int8 queries (q8, q_scale as
+ * in mqa_decode_q8). */
+int mqa_decode_append_q8(const int8_t* q8, const float* q_scale, const mqa_kv_cache* kv,
+                         const float* k_new, const float* v_new,
+                         const int32_t* seq_lens, int32_t max_seq_len,
+                         int32_t B, int32_t Hq, int32_t D, int32_t window,
+                         float softmax_scale, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mqa_status_string(int status);
 

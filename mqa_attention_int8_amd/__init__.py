@@ -8,4 +8,5 @@ from .binding import (KVView, MQAError, append_kv, kv_quantize_int8, load_librar
                       mqa_status_string, default_softmax_scale, library_path,
                       decode_workspace, mqa_prefill_workspace_bytes, prefill_workspace,
                       PagedKV, kv_quantize_int8_paged, mqa_decode_paged, mqa_decode_append_paged,
-                      mqa_decode_paged_workspace_bytes, mqa_prefill_chunk_paged)
+                      mqa_decode_paged_workspace_bytes, mqa_prefill_chunk_paged, mqa_decode_q8,
+                      mqa_decode_append_q8)

@@ -90,6 +90,12 @@ def load_library() -> ctypes.CDLL:
         lib.mqa_prefill_chunk_paged.argtypes = [vp, pg, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp,
                                                 ctypes.c_size_t, vp]
         lib.mqa_prefill_chunk_paged.restype = ctypes.c_int
+        lib.mqa_decode_q8.argtypes = [vp, vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32, f32, vp,
+                                      vp, ctypes.c_size_t, vp]
+        lib.mqa_decode_q8.restype = ctypes.c_int
+        lib.mqa_decode_append_q8.argtypes = [vp, vp, ctypes.POINTER(mqa_kv_cache), vp, vp, vp, i32, i32, i32, i32,
+                                             i32, f32, vp, vp, ctypes.c_size_t, vp]
+        lib.mqa_decode_append_q8.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -410,6 +416,57 @@ def mqa_prefill_chunk_paged(q: torch.Tensor, kv: PagedKV, prefix_lens: torch.Ten
                                        Hq, D, int(window), scale, _ptr(out), _ptr(workspace), ws_bytes,
                                        _stream(stream)),
            "mqa_prefill_chunk_paged")
+    return out
+
+
+def _q8_args(q8, q_scale, seq_lens, max_seq_len, window, softmax_scale, out, workspace):
+    _need(q8, torch.int8, "q8", 3)
+    _need(q_scale, torch.float32, "q_scale", 2)
+    _need(seq_lens, torch.int32, "seq_lens", 1)
+    B, Hq, D = (int(x) for x in q8.shape)
+    if tuple(q_scale.shape) != (B, Hq):
+        raise ValueError(f"q_scale must have shape {(B, Hq)}")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q8.device)
+    _need(out, torch.float32, "out", 3)
+    if workspace is None and mqa_decode_workspace_bytes(B, Hq, D, max_seq_len, window) > 0:
+        workspace = decode_workspace(B, Hq, D, max_seq_len, window, q8.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
+    return B, Hq, D, out, workspace, ws_bytes, scale
+
+
+def mqa_decode_q8(q8: torch.Tensor, q_scale: torch.Tensor, kv: KVView, seq_lens: torch.Tensor, max_seq_len: int,
+                  window: int, softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode step with int8 queries: q8 int8 [B, Hq, D], q_scale fp32 [B, Hq]."""
+    lib = load_library()
+    B, Hq, D, out, workspace, ws_bytes, scale = _q8_args(q8, q_scale, seq_lens, max_seq_len, window,
+                                                         softmax_scale, out, workspace)
+    view = kv.c_view()
+    _check(lib.mqa_decode_q8(_ptr(q8), _ptr(q_scale), ctypes.byref(view), _ptr(seq_lens), int(max_seq_len), B, Hq,
+                             D, int(window), scale, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
+           "mqa_decode_q8")
+    return out
+
+
+def mqa_decode_append_q8(q8: torch.Tensor, q_scale: torch.Tensor, kv: KVView, k_new: torch.Tensor,
+                         v_new: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, window: int,
+                         softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mqa_decode_append with int8 queries."""
+    lib = load_library()
+    B, Hq, D, out, workspace, ws_bytes, scale = _q8_args(q8, q_scale, seq_lens, max_seq_len, window,
+                                                         softmax_scale, out, workspace)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, torch.float32, n, 2)
+        if tuple(t.shape) != (B, D):
+            raise ValueError(f"{n} must have shape {(B, D)}")
+    cache = kv.c_cache()
+    _check(lib.mqa_decode_append_q8(_ptr(q8), _ptr(q_scale), ctypes.byref(cache), _ptr(k_new), _ptr(v_new),
+                                    _ptr(seq_lens), int(max_seq_len), B, Hq, D, int(window), scale, _ptr(out),
+                                    _ptr(workspace), ws_bytes, _stream(stream)),
+           "mqa_decode_append_q8")
     return out
 
 

@@ -267,6 +267,57 @@ int mqa_decode_append_paged(const uint16_t* q, const mqa_kv_paged* kv, const flo
                            out, workspace, workspace_bytes, stream);
 }
 
+namespace {
+int decode_q8_impl(const int8_t* q8, const float* q_scale, const mqa_kv_view& view, const mqa_kv_cache* cache,
+                   const float* k_new, const float* v_new, const int32_t* seq_lens, int32_t max_seq_len, int32_t B,
+                   int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!q8 || !q_scale || !seq_lens || !out) return MQA_ERR_NULL;
+  int st = check_decode_shape(B, Hq, D, max_seq_len);
+  if (st != MQA_OK) return st;
+  st = check_kv(&view, D);
+  if (st != MQA_OK) return st;
+  if (max_seq_len > view.L_cap) return MQA_ERR_SHAPE;
+  if (!aligned16(q8) || ((uintptr_t)q_scale & 3u) || !aligned16(out)) return MQA_ERR_ALIGN;
+  if ((view.L_cap & 3) || !aligned16(view.k_scale) || !aligned16(view.v_scale)) return MQA_ERR_ALIGN;
+  if (cache) {
+    if (!k_new || !v_new) return MQA_ERR_NULL;
+    if (((uintptr_t)k_new & 3u) || ((uintptr_t)v_new & 3u)) return MQA_ERR_ALIGN;
+  }
+  const mqa::DecodePlan plan = mqa::plan_decode(B, Hq, D, max_seq_len, window, device_cu_count());
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+  }
+  const mqa::QueryInt8 qi{q8, q_scale};
+  if (cache) {
+    const mqa::AppendRows rows{k_new, v_new, cache->k, cache->v, cache->k_scale, cache->v_scale};
+    return mqa::launch_decode(nullptr, view, mqa::KVLayout{}, seq_lens, B, Hq, D, window, softmax_scale, out,
+                              workspace, plan, static_cast<hipStream_t>(stream), &rows, &qi);
+  }
+  return mqa::launch_decode(nullptr, view, mqa::KVLayout{}, seq_lens, B, Hq, D, window, softmax_scale, out,
+                            workspace, plan, static_cast<hipStream_t>(stream), nullptr, &qi);
+}
+}  // namespace
+
+int mqa_decode_q8(const int8_t* q8, const float* q_scale, const mqa_kv_view* kv, const int32_t* seq_lens,
+                  int32_t max_seq_len, int32_t B, int32_t Hq, int32_t D, int32_t window, float softmax_scale,
+                  float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kv) return MQA_ERR_NULL;
+  return decode_q8_impl(q8, q_scale, *kv, nullptr, nullptr, nullptr, seq_lens, max_seq_len, B, Hq, D, window,
+                        softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int mqa_decode_append_q8(const int8_t* q8, const float* q_scale, const mqa_kv_cache* kv, const float* k_new,
+                         const float* v_new, const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq,
+                         int32_t D, int32_t window, float softmax_scale, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!kv) return MQA_ERR_NULL;
+  const mqa_kv_view view{kv->k, kv->v, kv->k_scale, kv->v_scale, kv->L_cap};
+  return decode_q8_impl(q8, q_scale, view, kv, k_new, v_new, seq_lens, max_seq_len, B, Hq, D, window,
+                        softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
 int mqa_prefill_chunk_paged(const uint16_t* q, const mqa_kv_paged* kv, const int32_t* prefix_lens,
                             int32_t max_prefix_len, int32_t B, int32_t C, int32_t Hq, int32_t D, int32_t window,
                             float softmax_scale, float* out, void* workspace, size_t workspace_bytes,

@@ -28,6 +28,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 // v_mfma_f32_16x16x32_f16, same lane layout as the bf16 form.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// int8 x int8 -> int32, 16x16x64: each lane supplies 16 bytes of A and of B.
+__device__ __forceinline__ i32x4 mfma16_i8(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma16_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

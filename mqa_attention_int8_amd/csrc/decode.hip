@@ -77,6 +77,10 @@ constexpr int kValueHeadroom = 7;
 
 struct DecodeParams {
   const uint16_t* q;
+  // int8 queries (q == nullptr): codes [B, Hq, D] and one fp32 scale per
+  // (token, head) row.
+  const int8_t* q8;
+  const float* q_scale;
   const int8_t* k;
   const int8_t* v;
   const float* ks;
@@ -213,27 +217,56 @@ __device__ __forceinline__ void rebase(WaveState<D, NT>& st, int nt, const f32x4
 // (at most two per sequence) gives the keys outside it weight zero; the
 // branch is wave-uniform and the empty asm keeps the compiler from turning it
 // into selects executed for every tile.
+// Q^T as an MFMA B operand. Q8 = false: q in fp16, scaled per wave by a
+// power of two. Q8 = true: the int8 codes of each (token, head) row as 16-byte
+// slices matching the K bytes a lane holds, and the row's scale per lane.
+template <int D, int NT, bool Q8>
+struct QOperand {
+  f16x8 h[NT][D / 32];
+};
 template <int D, int NT>
+struct QOperand<D, NT, true> {
+  u32x4 b[NT][D / 64];
+  float scale[NT];
+};
+
+template <int D, int NT, bool Q8>
 __device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
-                                             const f16x8 (&qop)[NT][D / 32],
+                                             const QOperand<D, NT, Q8>& qop,
                                              float kscale, int base, int lo, int hi, int g) {
   constexpr int KK = D / 32;
   constexpr int DPL = D / 16;
   const bool masked = (base < lo) || (base + kTileKeys > hi);  // wave-uniform
 
-  // ---- S^T = K Q'^T (fp16 operands, exact products, fp32 sums) ------------
   f32x4 s[2][NT];
+  if constexpr (!Q8) {
+    // ---- S^T = K Q'^T (fp16 operands, exact products, fp32 sums) ----------
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
+    for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) s[hf][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) s[hf][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 w = cur.k[hf][kk >> 1];
-      const f16x8 kop = as_f16x8(cat(i8x4_to_f16(w[2 * (kk & 1)]), i8x4_to_f16(w[2 * (kk & 1) + 1])));
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 w = cur.k[hf][kk >> 1];
+        const f16x8 kop = as_f16x8(cat(i8x4_to_f16(w[2 * (kk & 1)]), i8x4_to_f16(w[2 * (kk & 1) + 1])));
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s[hf][nt] = mfma16_f16(kop, qop[nt][kk], s[hf][nt]);
+        for (int nt = 0; nt < NT; ++nt) s[hf][nt] = mfma16_f16(kop, qop.h[nt][kk], s[hf][nt]);
+      }
     }
+  } else {
+    // ---- S^T = K8 Q8^T on int8 MFMA: the raw K bytes are the A operand; the
+    // int32 sums (|sum| <= D * 127 * 127 < 2^24) convert to fp32 exactly and
+    // take the row's q scale.
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < D / 64; ++w) acc = mfma16_i8(cur.k[hf][w], qop.b[nt][w], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[hf][nt][r] = (float)acc[r] * qop.scale[nt];
+      }
   }
 
   // ---- online softmax (log2 domain); P'' = 2^(z - m) s_v as fp16 hi + lo ----
@@ -406,9 +439,9 @@ __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D /
 // Each wave keeps two tiles in registers: on entry `ta` holds the loads of its
 // tile ia and `tb` those of ib (> ia); a buffer is refilled with the next
 // handed-out tile as soon as it has been consumed.
-template <int D, int NT, typename Load>
+template <int D, int NT, bool Q8, typename Load>
 __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D, NT>& st, const Load& load,
-                                          const f16x8 (&qop)[NT][D / 32], float kscale,
+                                          const QOperand<D, NT, Q8>& qop, float kscale,
                                           int pt0, int count, int ia, int ib, int* next, int lane, int lo, int hi,
                                           int g, int new_tile, const float (&xk)[D / 64], const float (&xv)[D / 64],
                                           int8_t* scratch, bool write, int8_t* krow, int8_t* vrow, float* ks,
@@ -424,13 +457,13 @@ __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D,
   while (ia < count) {
     if (ia == new_tile)
       encode_new_row<D>(ta, xk, xv, scratch, hi - 1 - (pt0 + ia) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
-    compute_tile<D, NT>(ta, st, qop, kscale, (pt0 + ia) * kTileKeys, lo, hi, g);
+    compute_tile<D, NT, Q8>(ta, st, qop, kscale, (pt0 + ia) * kTileKeys, lo, hi, g);
     ia = grab();
     load(ta, ia);
     if (ib >= count) break;
     if (ib == new_tile)
       encode_new_row<D>(tb, xk, xv, scratch, hi - 1 - (pt0 + ib) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
-    compute_tile<D, NT>(tb, st, qop, kscale, (pt0 + ib) * kTileKeys, lo, hi, g);
+    compute_tile<D, NT, Q8>(tb, st, qop, kscale, (pt0 + ib) * kTileKeys, lo, hi, g);
     ib = grab();
     load(tb, ib);
   }
@@ -439,7 +472,8 @@ __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D,
 // WINDOWED: the layer attends to the last `window` keys (the partition's
 // tiles then depend on the sequence length); otherwise to all of them.
 // PAGED: the cache is a block pool addressed through p.table.
-template <int D, int NT, bool WINDOWED, bool PAGED>
+// Q8: int8 queries (p.q8, p.q_scale) and int8 MFMA for Q K^T.
+template <int D, int NT, bool WINDOWED, bool PAGED, bool Q8>
 __global__ __launch_bounds__(64 * kWavesPerWG) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partition_kernel(DecodeParams p) {
   static_assert(NT == 1 || NT == 2, "a work-group serves at most 32 heads");
@@ -499,13 +533,26 @@ void decode_partition_kernel(DecodeParams p) {
   // before it).
   const int n_raw = (int)buf_load4(make_rsrc(p.seq_lens + b, 4), 0, 0);
   u32x4 qraw[NT][KK];
-  {
+  QOperand<D, NT, Q8> qop;
+  if constexpr (!Q8) {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + ((int64_t)b * Hq + h0) * D, (uint32_t)(Hg * D * 2));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         qraw[nt][kk] = buf_load16(qr, (uint32_t)(((16 * nt + c) * D + g * (D / 4) + 8 * kk) * 2), 0);
+  } else {
+    // lane (g, c): bytes g*D/4 + 16w .. +15 of row 16nt + c, the same
+    // contraction indices as the K bytes it holds
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q8 + ((int64_t)b * Hq + h0) * D, (uint32_t)(Hg * D));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.q_scale + (int64_t)b * Hq + h0, (uint32_t)(Hg * 4));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int w = 0; w < D / 64; ++w)
+        qop.b[nt][w] = buf_load16(qr, (uint32_t)((16 * nt + c) * D + g * (D / 4) + 16 * w), 0);
+      qop.scale[nt] = __uint_as_float(buf_load4(sr, (uint32_t)(16 * nt + c) * 4, 0));
+    }
   }
   // fused append: lane holds elements [D/64 * lane, D/64 * (lane + 1)) of the new K and V rows
   const bool appending = p.k_new != nullptr;
@@ -579,9 +626,8 @@ void decode_partition_kernel(DecodeParams p) {
   // Q^T as the B operand in fp16: the wave scales q by an exact power of two
   // that puts its largest |q| in [2^14, 2^15) and folds the scale into its
   // per-key logit factor (waves may differ; each works with true logits).
-  f16x8 qop[NT][KK];
-  float kscale;
-  {
+  float kscale = p.scale_log2;
+  if constexpr (!Q8) {
     float qmax = 0.f;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -603,7 +649,7 @@ void decode_partition_kernel(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           w[e] = cvt_pk_f16(bf16_lo_to_f32(qraw[nt][kk][e]) * qup, bf16_hi_to_f32(qraw[nt][kk][e]) * qup);
-        qop[nt][kk] = as_f16x8(w);
+        qop.h[nt][kk] = as_f16x8(w);
       }
   }
 
@@ -617,7 +663,7 @@ void decode_partition_kernel(DecodeParams p) {
   }
   st.vexp = -1000;
 
-  run_tiles<D, NT>(ta, tb, st, load, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g,
+  run_tiles<D, NT, Q8>(ta, tb, st, load, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g,
                    new_tile, xk, xv, sm_new[wave], blockIdx.z == 0, p.k_w + new_row * D, p.v_w + new_row * D,
                    p.ks_w + new_row, p.vs_w + new_row);
 
@@ -740,25 +786,28 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
   *reinterpret_cast<f32x4*>(out + ((int64_t)b * Hq + h) * D + d0) = acc * inv;
 }
 
-template <int D, int NT, bool PAGED>
+template <int D, int NT, bool PAGED, bool Q8>
 void launch_partitions(const DecodeParams& prm, int B, hipStream_t stream) {
   const dim3 block(64 * kWavesPerWG);
   const dim3 grid(prm.num_parts, B, (prm.Hq + kHeadsPerGroup - 1) / kHeadsPerGroup);
   if (prm.window > 0)
-    hipLaunchKernelGGL((decode_partition_kernel<D, NT, true, PAGED>), grid, block, 0, stream, prm);
+    hipLaunchKernelGGL((decode_partition_kernel<D, NT, true, PAGED, Q8>), grid, block, 0, stream, prm);
   else
-    hipLaunchKernelGGL((decode_partition_kernel<D, NT, false, PAGED>), grid, block, 0, stream, prm);
+    hipLaunchKernelGGL((decode_partition_kernel<D, NT, false, PAGED, Q8>), grid, block, 0, stream, prm);
 }
 
 template <int D>
 void launch_by_heads(const DecodeParams& prm, int B, hipStream_t stream) {
-  const bool paged = prm.table != nullptr;
+  // int8 queries are served on contiguous buffers only
+  const bool paged = prm.table != nullptr, q8 = prm.q8 != nullptr;
   if (prm.Hq <= 16) {
-    if (paged) launch_partitions<D, 1, true>(prm, B, stream);
-    else launch_partitions<D, 1, false>(prm, B, stream);
+    if (q8) launch_partitions<D, 1, false, true>(prm, B, stream);
+    else if (paged) launch_partitions<D, 1, true, false>(prm, B, stream);
+    else launch_partitions<D, 1, false, false>(prm, B, stream);
   } else {
-    if (paged) launch_partitions<D, 2, true>(prm, B, stream);
-    else launch_partitions<D, 2, false>(prm, B, stream);
+    if (q8) launch_partitions<D, 2, false, true>(prm, B, stream);
+    else if (paged) launch_partitions<D, 2, true, false>(prm, B, stream);
+    else launch_partitions<D, 2, false, false>(prm, B, stream);
   }
 }
 
@@ -801,8 +850,11 @@ DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, in
 
 int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layout, const int32_t* seq_lens,
                   int32_t B, int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
-                  void* workspace, const DecodePlan& plan, hipStream_t stream, const AppendRows* append) {
+                  void* workspace, const DecodePlan& plan, hipStream_t stream, const AppendRows* append,
+                  const QueryInt8* q8) {
   DecodeParams prm;
+  prm.q8 = q8 ? q8->codes : nullptr;
+  prm.q_scale = q8 ? q8->scale : nullptr;
   prm.table = layout.table;
   prm.table_len = layout.table_len;
   prm.log2_bs = layout.log2_bs;

@@ -51,10 +51,17 @@ struct AppendRows {
   float* v_scale;
 };
 
+// int8 queries: codes [B, Hq, D] and one fp32 scale per (token, head) row.
+struct QueryInt8 {
+  const int8_t* codes;
+  const float* scale;
+};
+
+// q == nullptr with q8 set: the int8-query variant.
 int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layout, const int32_t* seq_lens,
                   int32_t B, int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
                   void* workspace, const DecodePlan& plan, hipStream_t stream,
-                  const AppendRows* append = nullptr);
+                  const AppendRows* append = nullptr, const QueryInt8* q8 = nullptr);
 
 size_t prefill_workspace_bytes(int32_t B, int32_t C, int32_t D, int32_t max_prefix_len);
 

@@ -175,7 +175,21 @@ def decode_ref(q_bits, k_q, k_s, v_q, v_s, seq_lens, window, softmax_scale=None)
     k_s/v_s fp32 [B, L_cap]; seq_lens [B] (keys including the new token);
     window <= 0 means global. Returns float64 [B, Hq, D].
     """
-    q = bf16_bits_to_f64(q_bits)
+    return _decode_f64(bf16_bits_to_f64(q_bits), k_q, k_s, v_q, v_s, seq_lens, window, softmax_scale)
+
+
+def decode_ref_q8(q8, q_scale, k_q, k_s, v_q, v_s, seq_lens, window, softmax_scale=None):
+    """Decode step with int8 queries [explinks.com page, 训练和服务的量化:
+    activations in int8 too; int8 内核实现: int8 attention kernels].
+
+    q8 int8 [B, Hq, D] with one fp32 scale per (token, head) row, q_scale
+    [B, Hq]: the query is the dequantized row q8 * q_scale, so every logit is
+    softmax_scale * q_scale * k_scale * (q8 . k8). Otherwise as ``decode_ref``.
+    """
+    return _decode_f64(dequantize_rows(q8, q_scale), k_q, k_s, v_q, v_s, seq_lens, window, softmax_scale)
+
+
+def _decode_f64(q, k_q, k_s, v_q, v_s, seq_lens, window, softmax_scale):
     B, Hq, D = q.shape
     sigma = _sigma(softmax_scale, D)
     out = np.zeros((B, Hq, D))

@@ -27,7 +27,8 @@ def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert {"kv_quantize_int8", "mqa_decode", "mqa_decode_append", "mqa_prefill_chunk",
             "mqa_decode_workspace_bytes", "mqa_status_string", "kv_quantize_int8_paged", "mqa_decode_paged",
-            "mqa_decode_append_paged", "mqa_prefill_chunk_paged", "mqa_decode_paged_workspace_bytes"} <= set(names)
+            "mqa_decode_append_paged", "mqa_prefill_chunk_paged", "mqa_decode_paged_workspace_bytes",
+            "mqa_decode_q8", "mqa_decode_append_q8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in mqa_int8.h but not exported"
 
@@ -220,4 +221,21 @@ def test_prefill_paged_validation(lib):
     assert pf(paged(), max_prefix=250, C=16, W=0) == 2          # global layer past the table
     assert pf(paged(), max_prefix=1000, C=16, W=242) == 2       # W + C - 1 = 257 > 256
     assert pf(paged(), max_prefix=64, C=16, ws=None, ws_bytes=0) == 5
+
+
+def test_decode_q8_validation(lib):
+    v = kv()
+    d = lambda **kw: lib.mqa_decode_q8(kw.get("q8", FAKE), kw.get("qs", FAKE), ctypes.byref(v), FAKE,
+                                       kw.get("max_len", 64), 2, kw.get("Hq", 8), kw.get("D", 128), 0, 0.1, FAKE,
+                                       None, 0, None)
+    assert d(q8=None) == 1
+    assert d(qs=None) == 1
+    assert d(q8=FAKE + 8) == 4
+    assert d(qs=FAKE + 2) == 4
+    assert d(D=96) == 3
+    assert d(Hq=65) == 3
+    assert d(max_len=65) == 2
+    c = __import__("mqa_attention_int8_amd").binding.mqa_kv_cache(FAKE, FAKE, FAKE, FAKE, 64)
+    assert lib.mqa_decode_append_q8(FAKE, FAKE, ctypes.byref(c), None, FAKE, FAKE, 64, 2, 8, 128, 0, 0.1, FAKE,
+                                    None, 0, None) == 1
 
