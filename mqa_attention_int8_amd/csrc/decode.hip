@@ -289,13 +289,16 @@ __device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
     }
   }
   // Value exponent: every s_v of the tile is below 2^(x - 126), x the largest
-  // biased exponent (s_v >= 0, so the bits compare as integers); uniform.
+  // biased exponent (s_v >= 0, so the bits compare as integers). Each lane
+  // checks its own keys; only when one of them needs a larger exponent is
+  // the tile's maximum formed (uniform).
   {
-    int x = 0;
+    uint32_t xb = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x = max(x, (int)(__float_as_uint(vscl[i]) >> 23));
-    x = __builtin_amdgcn_readfirstlane(quad_max_i(x)) - 126 - kValueHeadroom;
-    if (x > st.vexp) {  // rare: the accumulator moves to the new value scale
+    for (int i = 0; i < 8; ++i) xb = max(xb, __float_as_uint(vscl[i]));
+    int x = (int)(xb >> 23) - 126 - kValueHeadroom;
+    if (__builtin_amdgcn_ballot_w64(x > st.vexp) != 0) {  // rare: the accumulator moves to the new value scale
+      x = __builtin_amdgcn_readfirstlane(quad_max_i(x));
       const float f = __builtin_ldexpf(1.f, max(st.vexp - x, -200));
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -317,8 +320,9 @@ __device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
 #pragma unroll
       for (int i = 0; i < 8; ++i) t[i] = ok[i] ? t[i] : -INFINITY;
     }
-    const float tmax = quad_max(max8(t));
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > kLazy) != 0, 0))  // includes m = -inf
+    // any lane over the lazy bound (or m = -inf) sends the whole wave to rebase
+    const float tmax = max8(t);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > kLazy) != 0, 0))
       rebase<D, NT>(st, nt, s, kscl, ok, masked, t);
     u32x4 hw, lw;
 #pragma unroll
