@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the hybrid/long/prefill lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
-    ap.add_argument("--only", choices=["decode", "hybrid", "long", "prefill", "paged", "q8"], default=None,
+    ap.add_argument("--only", choices=["decode", "hybrid", "long", "prefill", "paged", "q8", "prefix_cache"],
+                    default=None,
                     help="time a single workload (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -363,6 +364,62 @@ def bench_q8(torch, m, acct, stream):
     return res
 
 
+def bench_prefix_cache(torch, m, stream):
+    """Host-memory prefix cache: restore (host pool -> device) and store
+    bandwidth of an 8192-token prefix over three shared KV buffers, and the
+    control plane on a synthetic multi-turn stream (conversations of ~180
+    messages, the pages' average; the hit rate is a property of this stream,
+    not a claim about real traffic)."""
+    import time
+    import numpy as np
+    B, D, bs, L, nb = 4, 128, 32, 8192, 3
+    bufs = [m.KVView.empty(B, L, D) for _ in range(nb)]
+    for kv in bufs:
+        kv.k.random_(-127, 128)
+        kv.v.random_(-127, 128)
+        kv.k_scale.uniform_(0, 0.03)
+        kv.v_scale.uniform_(0, 0.03)
+    n_blocks = L // bs
+    pool = m.host_pool(n_blocks, nb, bs, D)
+    slots = np.arange(n_blocks, dtype=np.int64)
+    nbytes = n_blocks * m.kv_block_bytes(nb, bs, D)
+    res = {"prefix_tokens": L, "buffers": nb, "block_size": bs, "bytes": nbytes}
+    timer = Timer(torch, stream)
+    with torch.cuda.stream(stream):
+        for name, fn in (("store", m.mqa_kv_blocks_to_host), ("restore", m.mqa_kv_blocks_to_device)):
+            for _ in range(3):
+                fn(bufs, 1, 0, slots, bs, pool, stream=stream)
+            torch.cuda.synchronize()
+            reps = 20
+            timer.start()
+            for _ in range(reps):
+                fn(bufs, 1, 0, slots, bs, pool, stream=stream)
+            ms = timer.stop_ms() / reps
+            res[name + "_us"] = ms * 1e3
+            res[name + "_GBps"] = nbytes / (ms * 1e-3) / 1e9
+    # control plane on a synthetic stream
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import synth
+    g = synth.rng(990, 1)
+    n_conv, turns = 64, 90                      # 2 messages per turn: ~180 messages per conversation
+    cache = m.PrefixCache(16, 1 << 18)
+    hist = [[] for _ in range(n_conv)]
+    order = [c for _ in range(turns) for c in g.permutation(n_conv)]
+    t0 = time.perf_counter()
+    for c in order:
+        req = hist[c] + g.integers(0, 32000, size=int(g.integers(8, 64))).tolist()
+        cache.match(req)
+        hist[c] = req + g.integers(0, 32000, size=int(g.integers(8, 64))).tolist()
+        cache.insert(hist[c])
+    dt = time.perf_counter() - t0
+    st = cache.stats()
+    cache.close()
+    res["control_plane_us_per_turn"] = dt / len(order) * 1e6
+    res["synthetic_stream_token_hit_rate"] = st["matched_tokens"] / max(1, st["lookup_tokens"])
+    res["synthetic_stream"] = f"{n_conv} conversations x {turns} turns, messages 8-63 tokens, block 16"
+    return res
+
+
 def bench_prefill(torch, m, acct, stream):
     B, C, P, Hq, D = 16, 512, 8192, 32, 128
     gen = torch.Generator(device="cuda")
@@ -481,6 +538,8 @@ def main():
             extra["paged"] = bench_paged(torch, m, acct, stream)
         if args.only in (None, "q8"):
             extra["q8"] = bench_q8(torch, m, acct, stream)
+        if args.only in (None, "prefix_cache"):
+            extra["prefix_cache"] = bench_prefix_cache(torch, m, stream)
     if dec is None:
         print(json.dumps({"extra": extra}))
         return

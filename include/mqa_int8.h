@@ -301,6 +301,85 @@ int mqa_decode_append_q8(const int8_t* q8, const float* q_scale, const mqa_kv_ca
                          float softmax_scale, float* out, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Host-memory prefix cache between conversation turns.
+ * [9c1h.cn page "秘訣2": the KV of each conversation's prefix and generated
+ * messages stays in host memory for later turns; a tree-structured LRU
+ * cache, looked up by a rolling hash of the prefix tokens, returns the
+ * longest matching cached prefix, and partial matches hit too. explinks.com
+ * page, sections "有状态缓存" and "LRU 缓存结构", the same.]
+ *
+ * Control plane (host only, no HIP calls): the cache tracks which token
+ * prefixes are cached, block by block (block_size tokens), each block in one
+ * slot of a host pool the CALLER allocates (pinned, device-accessible); the
+ * cache object itself owns only its bookkeeping. A block is identified by the
+ * rolling hash of the whole prefix up to its end and verified token by token
+ * against its parent chain, so a hash collision never returns wrong KV.
+ * Eviction removes the least recently used leaf block (one no cached block
+ * extends), so every cached block's prefix is cached; match and insert count
+ * as a use of every block on their chain, oldest first. Not thread-safe: one
+ * caller at a time.
+ * Data plane: mqa_kv_blocks_to_host / _to_device copy whole blocks of one
+ * sequence between device KV buffers (every buffer the model shares, in one
+ * launch) and pool slots.
+ * ------------------------------------------------------------------------- */
+typedef struct mqa_prefix_cache mqa_prefix_cache;
+
+typedef struct {
+  int64_t capacity_blocks;
+  int64_t used_blocks;
+  int64_t lookups;          /* mqa_prefix_cache_match calls              */
+  int64_t lookup_tokens;    /* tokens offered to them                     */
+  int64_t matched_tokens;   /* tokens they found cached                   */
+  int64_t inserted_blocks;
+  int64_t evicted_blocks;
+} mqa_prefix_cache_stats;
+
+/* Create a cache of capacity_blocks slots of block_size tokens.
+ * Errors: NULL, SHAPE. */
+int mqa_prefix_cache_create(int32_t block_size, int64_t capacity_blocks, mqa_prefix_cache** out);
+void mqa_prefix_cache_destroy(mqa_prefix_cache* cache);
+
+/* Longest cached prefix of tokens[0, n_tokens) (host array): *matched_tokens
+ * is a multiple of block_size; slots (host, room for n_tokens / block_size
+ * entries, may be NULL) receives the pool slot of each matched block. */
+int mqa_prefix_cache_match(mqa_prefix_cache* cache, const int32_t* tokens, int64_t n_tokens,
+                           int64_t* matched_tokens, int64_t* slots);
+
+/* Cache every full block of tokens[0, n_tokens): blocks already cached are
+ * reused, the others get slots (evicting least recently used leaves as
+ * needed). On return slots[0, *n_blocks) hold the slot of each block and
+ * blocks [*first_new_block, *n_blocks) are new: the caller copies their KV
+ * into those slots (mqa_kv_blocks_to_host) before any later match may read
+ * them. *n_blocks < n_tokens / block_size only when the cache is too small
+ * for the whole chain. */
+int mqa_prefix_cache_insert(mqa_prefix_cache* cache, const int32_t* tokens, int64_t n_tokens,
+                            int64_t* slots, int64_t* first_new_block, int64_t* n_blocks);
+
+int mqa_prefix_cache_get_stats(const mqa_prefix_cache* cache, mqa_prefix_cache_stats* out);
+
+/* Copy blocks first_block .. first_block+n_blocks-1 (positions
+ * block * block_size ...) of sequence b (0 <= b < B, the buffers' batch) of
+ * each of the n_bufs buffers (host array of views, 1 <= n_bufs <= 8,
+ * head_dim D) into pool slots
+ * slots[0..n_blocks) (host array), or back. Slot layout, for each buffer in
+ * order: K rows [block_size, D] int8, V rows, K scales [block_size] fp32, V
+ * scales; a slot is n_bufs * block_size * (2D + 8) bytes. host_pool: pinned
+ * host memory from the HIP runtime (hipHostMalloc or an allocator built on
+ * it; the call fails with MQA_ERR_HIP for memory the runtime cannot map for
+ * the device) of pool_slots slots, 16-byte aligned.
+ * block_size a multiple of 16; the blocks must lie inside every buffer
+ * (first_block + n_blocks) * block_size <= L_cap. Asynchronous on the stream
+ * (the pool must stay valid and unchanged until the copy has run).
+ * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, HIP. */
+int mqa_kv_blocks_to_host(const mqa_kv_view* bufs, int32_t n_bufs, int32_t B, int32_t b,
+                          int64_t first_block, int64_t n_blocks, int32_t block_size, int32_t D,
+                          const int64_t* slots, void* host_pool, int64_t pool_slots, void* stream);
+int mqa_kv_blocks_to_device(const mqa_kv_cache* bufs, int32_t n_bufs, int32_t B, int32_t b,
+                            int64_t first_block, int64_t n_blocks, int32_t block_size, int32_t D,
+                            const int64_t* slots, const void* host_pool, int64_t pool_slots,
+                            void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mqa_status_string(int status);
 

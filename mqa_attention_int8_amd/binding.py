@@ -46,6 +46,11 @@ class mqa_kv_paged(ctypes.Structure):
                 ("table_len", ctypes.c_int32), ("num_blocks", ctypes.c_int32)]
 
 
+class mqa_prefix_cache_stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("capacity_blocks", "used_blocks", "lookups", "lookup_tokens",
+                                              "matched_tokens", "inserted_blocks", "evicted_blocks")]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -96,6 +101,23 @@ def load_library() -> ctypes.CDLL:
         lib.mqa_decode_append_q8.argtypes = [vp, vp, ctypes.POINTER(mqa_kv_cache), vp, vp, vp, i32, i32, i32, i32,
                                              i32, f32, vp, vp, ctypes.c_size_t, vp]
         lib.mqa_decode_append_q8.restype = ctypes.c_int
+        i64, p64 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)
+        lib.mqa_prefix_cache_create.argtypes = [i32, i64, ctypes.POINTER(vp)]
+        lib.mqa_prefix_cache_create.restype = ctypes.c_int
+        lib.mqa_prefix_cache_destroy.argtypes = [vp]
+        lib.mqa_prefix_cache_destroy.restype = None
+        lib.mqa_prefix_cache_match.argtypes = [vp, vp, i64, p64, vp]
+        lib.mqa_prefix_cache_match.restype = ctypes.c_int
+        lib.mqa_prefix_cache_insert.argtypes = [vp, vp, i64, vp, p64, p64]
+        lib.mqa_prefix_cache_insert.restype = ctypes.c_int
+        lib.mqa_prefix_cache_get_stats.argtypes = [vp, ctypes.POINTER(mqa_prefix_cache_stats)]
+        lib.mqa_prefix_cache_get_stats.restype = ctypes.c_int
+        lib.mqa_kv_blocks_to_host.argtypes = [ctypes.POINTER(mqa_kv_view), i32, i32, i32, i64, i64, i32, i32, vp,
+                                              vp, i64, vp]
+        lib.mqa_kv_blocks_to_host.restype = ctypes.c_int
+        lib.mqa_kv_blocks_to_device.argtypes = [ctypes.POINTER(mqa_kv_cache), i32, i32, i32, i64, i64, i32, i32, vp,
+                                                vp, i64, vp]
+        lib.mqa_kv_blocks_to_device.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -468,6 +490,103 @@ def mqa_decode_append_q8(q8: torch.Tensor, q_scale: torch.Tensor, kv: KVView, k_
                                     _ptr(workspace), ws_bytes, _stream(stream)),
            "mqa_decode_append_q8")
     return out
+
+
+class PrefixCache:
+    """Host-memory prefix cache (control plane in libmqa_int8): which token
+    prefixes are cached, block by block, in which slots of a host pool."""
+
+    def __init__(self, block_size: int, capacity_blocks: int):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check(self._lib.mqa_prefix_cache_create(int(block_size), int(capacity_blocks), ctypes.byref(h)),
+               "mqa_prefix_cache_create")
+        self._h = h
+        self.block_size = int(block_size)
+        self.capacity_blocks = int(capacity_blocks)
+
+    @staticmethod
+    def _tokens(tokens):
+        import numpy as np
+        return np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+
+    def match(self, tokens):
+        """(matched_tokens, slots of the matched blocks)."""
+        import numpy as np
+        t = self._tokens(tokens)
+        slots = np.zeros(max(1, len(t) // self.block_size), np.int64)
+        m = ctypes.c_int64()
+        _check(self._lib.mqa_prefix_cache_match(self._h, t.ctypes.data, len(t), ctypes.byref(m), slots.ctypes.data),
+               "mqa_prefix_cache_match")
+        return int(m.value), slots[: int(m.value) // self.block_size].copy()
+
+    def insert(self, tokens):
+        """(slots of the blocks, first new block, number of blocks cached)."""
+        import numpy as np
+        t = self._tokens(tokens)
+        slots = np.zeros(max(1, len(t) // self.block_size), np.int64)
+        first, n = ctypes.c_int64(), ctypes.c_int64()
+        _check(self._lib.mqa_prefix_cache_insert(self._h, t.ctypes.data, len(t), slots.ctypes.data,
+                                                 ctypes.byref(first), ctypes.byref(n)), "mqa_prefix_cache_insert")
+        return slots[: n.value].copy(), int(first.value), int(n.value)
+
+    def stats(self) -> dict:
+        st = mqa_prefix_cache_stats()
+        _check(self._lib.mqa_prefix_cache_get_stats(self._h, ctypes.byref(st)), "mqa_prefix_cache_get_stats")
+        return {n: int(getattr(st, n)) for n, _ in mqa_prefix_cache_stats._fields_}
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.mqa_prefix_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+
+def kv_block_bytes(n_bufs: int, block_size: int, D: int) -> int:
+    return n_bufs * block_size * (2 * D + 8)
+
+
+def host_pool(n_slots: int, n_bufs: int, block_size: int, D: int) -> torch.Tensor:
+    """Pinned host memory for n_slots cached blocks (allocated pinned)."""
+    return torch.empty(n_slots * kv_block_bytes(n_bufs, block_size, D), dtype=torch.uint8, pin_memory=True)
+
+
+def _pool_slots(pool: torch.Tensor, n_bufs: int, block_size: int, D: int) -> int:
+    if pool.dtype != torch.uint8 or pool.is_cuda or not pool.is_pinned() or not pool.is_contiguous():
+        raise ValueError("host_pool must be a contiguous pinned uint8 host tensor")
+    return pool.numel() // kv_block_bytes(n_bufs, block_size, D)
+
+
+def mqa_kv_blocks_to_host(bufs, b: int, first_block: int, slots, block_size: int, pool: torch.Tensor,
+                          stream=None) -> None:
+    """Copy blocks first_block.. of sequence b of every buffer into pool slots."""
+    import numpy as np
+    lib = load_library()
+    views = (mqa_kv_view * len(bufs))(*[kv.c_view() for kv in bufs])
+    s = np.ascontiguousarray(np.asarray(slots, np.int64))
+    D = bufs[0].D
+    if not 0 <= int(b) < bufs[0].B or any(kv.B != bufs[0].B or kv.D != D for kv in bufs):
+        raise ValueError("mqa_kv_blocks_to_host: sequence index or buffer shapes")
+    _check(lib.mqa_kv_blocks_to_host(views, len(bufs), bufs[0].B, int(b), int(first_block), len(s), int(block_size), D,
+                                     s.ctypes.data, pool.data_ptr(), _pool_slots(pool, len(bufs), block_size, D),
+                                     _stream(stream)), "mqa_kv_blocks_to_host")
+
+
+def mqa_kv_blocks_to_device(bufs, b: int, first_block: int, slots, block_size: int, pool: torch.Tensor,
+                            stream=None) -> None:
+    """Copy pool slots back into blocks first_block.. of sequence b of every buffer."""
+    import numpy as np
+    lib = load_library()
+    caches = (mqa_kv_cache * len(bufs))(*[kv.c_cache() for kv in bufs])
+    s = np.ascontiguousarray(np.asarray(slots, np.int64))
+    D = bufs[0].D
+    if not 0 <= int(b) < bufs[0].B or any(kv.B != bufs[0].B or kv.D != D for kv in bufs):
+        raise ValueError("mqa_kv_blocks_to_device: sequence index or buffer shapes")
+    _check(lib.mqa_kv_blocks_to_device(caches, len(bufs), bufs[0].B, int(b), int(first_block), len(s), int(block_size), D,
+                                       s.ctypes.data, pool.data_ptr(), _pool_slots(pool, len(bufs), block_size, D),
+                                       _stream(stream)), "mqa_kv_blocks_to_device")
 
 
 def hip_runtimes_mapped() -> list[str]:

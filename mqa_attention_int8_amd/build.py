@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libmqa_int8.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quantize.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "prefix_cache.cpp", "quantize.hip", "decode.hip", "prefill.hip", "kv_transfer.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -318,6 +318,54 @@ int mqa_decode_append_q8(const int8_t* q8, const float* q_scale, const mqa_kv_ca
                         softmax_scale, out, workspace, workspace_bytes, stream);
 }
 
+namespace {
+int check_transfer(const mqa_kv_view* bufs, int32_t n_bufs, int32_t B, int32_t b, int64_t first_block,
+                   int64_t n_blocks, int32_t block_size, int32_t D, const int64_t* slots, const void* pool,
+                   int64_t pool_slots) {
+  if (!bufs || !pool || (n_blocks > 0 && !slots)) return MQA_ERR_NULL;
+  if (n_bufs < 1 || n_bufs > 8 || B <= 0 || b < 0 || b >= B || first_block < 0 || n_blocks < 0 || pool_slots <= 0)
+    return MQA_ERR_SHAPE;
+  if (block_size <= 0 || block_size % 16 != 0) return MQA_ERR_SHAPE;
+  if (!supported_d(D)) return MQA_ERR_UNSUPPORTED;
+  if (!aligned16(pool)) return MQA_ERR_ALIGN;
+  for (int32_t i = 0; i < n_bufs; ++i) {
+    const mqa_kv_view& v = bufs[i];
+    if (!v.k || !v.v || !v.k_scale || !v.v_scale) return MQA_ERR_NULL;
+    if (v.L_cap <= 0 || (first_block + n_blocks) * (int64_t)block_size > v.L_cap) return MQA_ERR_SHAPE;
+    if (!aligned16(v.k) || !aligned16(v.v) || ((uintptr_t)v.k_scale & 3u) || ((uintptr_t)v.v_scale & 3u))
+      return MQA_ERR_ALIGN;
+  }
+  for (int64_t i = 0; i < n_blocks; ++i)
+    if (slots[i] < 0 || slots[i] >= pool_slots) return MQA_ERR_SHAPE;
+  return MQA_OK;
+}
+}  // namespace
+
+int mqa_kv_blocks_to_host(const mqa_kv_view* bufs, int32_t n_bufs, int32_t B, int32_t b, int64_t first_block,
+                          int64_t n_blocks, int32_t block_size, int32_t D, const int64_t* slots, void* host_pool,
+                          int64_t pool_slots, void* stream) {
+  const int st =
+      check_transfer(bufs, n_bufs, B, b, first_block, n_blocks, block_size, D, slots, host_pool, pool_slots);
+  if (st != MQA_OK || n_blocks == 0) return st;
+  return mqa::launch_kv_block_copy(false, bufs, n_bufs, b, first_block, n_blocks, block_size, D, slots, host_pool,
+                                   static_cast<hipStream_t>(stream));
+}
+
+int mqa_kv_blocks_to_device(const mqa_kv_cache* bufs, int32_t n_bufs, int32_t B, int32_t b, int64_t first_block,
+                            int64_t n_blocks, int32_t block_size, int32_t D, const int64_t* slots,
+                            const void* host_pool, int64_t pool_slots, void* stream) {
+  if (!bufs) return MQA_ERR_NULL;
+  if (n_bufs < 1 || n_bufs > 8) return MQA_ERR_SHAPE;
+  mqa_kv_view views[8];
+  for (int32_t i = 0; i < n_bufs; ++i)
+    views[i] = mqa_kv_view{bufs[i].k, bufs[i].v, bufs[i].k_scale, bufs[i].v_scale, bufs[i].L_cap};
+  const int st =
+      check_transfer(views, n_bufs, B, b, first_block, n_blocks, block_size, D, slots, host_pool, pool_slots);
+  if (st != MQA_OK || n_blocks == 0) return st;
+  return mqa::launch_kv_block_copy(true, views, n_bufs, b, first_block, n_blocks, block_size, D, slots,
+                                   const_cast<void*>(host_pool), static_cast<hipStream_t>(stream));
+}
+
 int mqa_prefill_chunk_paged(const uint16_t* q, const mqa_kv_paged* kv, const int32_t* prefix_lens,
                             int32_t max_prefix_len, int32_t B, int32_t C, int32_t Hq, int32_t D, int32_t window,
                             float softmax_scale, float* out, void* workspace, size_t workspace_bytes,

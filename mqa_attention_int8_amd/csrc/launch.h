@@ -63,6 +63,11 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layo
                   void* workspace, const DecodePlan& plan, hipStream_t stream,
                   const AppendRows* append = nullptr, const QueryInt8* q8 = nullptr);
 
+// Whole KV blocks of sequence b between device buffers and host pool slots.
+int launch_kv_block_copy(bool to_device, const mqa_kv_view* bufs, int32_t n_bufs, int32_t b, int64_t first_block,
+                         int64_t n_blocks, int32_t block_size, int32_t D, const int64_t* slots, void* pool,
+                         hipStream_t stream);
+
 size_t prefill_workspace_bytes(int32_t B, int32_t C, int32_t D, int32_t max_prefix_len);
 
 int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layout,

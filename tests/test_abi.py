@@ -239,3 +239,33 @@ def test_decode_q8_validation(lib):
     assert lib.mqa_decode_append_q8(FAKE, FAKE, ctypes.byref(c), None, FAKE, FAKE, 64, 2, 8, 128, 0, 0.1, FAKE,
                                     None, 0, None) == 1
 
+
+def test_kv_transfer_validation(lib):
+    from mqa_attention_int8_amd.binding import mqa_kv_view, mqa_kv_cache
+    views = (mqa_kv_view * 2)(kv(L_cap=256), kv(L_cap=256))
+    slots = (ctypes.c_int64 * 4)(0, 1, 2, 3)
+    t = lambda **kw: lib.mqa_kv_blocks_to_host(kw.get("views", views), kw.get("n_bufs", 2), kw.get("B", 2),
+                                               kw.get("b", 0), kw.get("first", 0),
+                                               kw.get("n", 4), kw.get("bs", 32), kw.get("D", 128),
+                                               kw.get("slots", slots), kw.get("pool", FAKE), kw.get("pool_slots", 8),
+                                               None)
+    assert t(pool=None) == 1
+    assert t(slots=None) == 1
+    assert t(n_bufs=0) == 2 and t(n_bufs=9) == 2
+    assert t(bs=24) == 2
+    assert t(first=5) == 2                  # (5 + 4) * 32 > L_cap
+    assert t(pool_slots=3) == 2             # slot 3 outside the pool
+    assert t(D=96) == 3
+    assert t(pool=FAKE + 8) == 4
+    assert t(b=2) == 2 and t(b=-1) == 2 and t(B=0) == 2
+    assert t(n=0) == 0                      # nothing to copy: no launch
+    caches = (mqa_kv_cache * 1)(mqa_kv_cache(FAKE, FAKE, FAKE, FAKE, 64))
+    assert lib.mqa_kv_blocks_to_device(caches, 1, 1, 0, 0, 4, 32, 128, slots, FAKE, 8, None) == 2  # 4 blocks > 64 rows
+
+
+def test_prefix_cache_create_validation(lib):
+    h = ctypes.c_void_p()
+    assert lib.mqa_prefix_cache_create(0, 10, ctypes.byref(h)) == 2
+    assert lib.mqa_prefix_cache_create(16, 0, ctypes.byref(h)) == 2
+    assert lib.mqa_prefix_cache_create(16, 10, None) == 1
+
