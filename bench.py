@@ -468,37 +468,45 @@ def cpu_baseline(budget_s: float):
     """The oracle (numpy, float64) on a bounded sample of the decode workload.
 
     Per sequence, the timed work is what one step does: encode the new token's
-    K and V rows, then the global and the window-1024 layer. The cache
-    contents are encoded beforehand, outside the timed region."""
+    K and V rows, then the global and the window-1024 layer. The 64
+    sequences' caches are encoded once, outside the timed region; steps over
+    them are repeated until about ``budget_s`` seconds of timed work."""
     import numpy as np
     from threadpoolctl import threadpool_info
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import oracle
     import synth
-    B, Hq, D, L = 64, 32, 128, 4096
-    done, t_work = 0, 0.0
+    B, Hq, D, L, n = 64, 32, 128, 4096, 4
     t_all = time.perf_counter()
-    while t_work < budget_s and done < B:
-        n = 4
-        k = synth.normal_f32(synth.rng(2, synth.T_K, 1000 + done), (n, L, D))
-        v = synth.normal_f32(synth.rng(2, synth.T_V, 1000 + done), (n, L, D))
-        q = synth.q_bf16(synth.rng(2, synth.T_Q, 1000 + done), (n, Hq, D))
-        lens = np.full(n, L, np.int32)
-        kq, ks = oracle.quantize_rows(k)
-        vq, vs = oracle.quantize_rows(v)
-        t0 = time.perf_counter()
-        kq[:, -1], ks[:, -1] = oracle.quantize_rows(k[:, -1])
-        vq[:, -1], vs[:, -1] = oracle.quantize_rows(v[:, -1])
-        for w in (0, 1024):
-            oracle.decode_ref(q, kq, ks, vq, vs, lens, w)
-        t_work += time.perf_counter() - t0
-        done += n
+    chunks = []
+    for c0 in range(0, B, n):
+        k = synth.normal_f32(synth.rng(2, synth.T_K, 1000 + c0), (n, L, D))
+        v = synth.normal_f32(synth.rng(2, synth.T_V, 1000 + c0), (n, L, D))
+        q = synth.q_bf16(synth.rng(2, synth.T_Q, 1000 + c0), (n, Hq, D))
+        kq, ks = oracle.quantize_rows(k[:, :-1])
+        vq, vs = oracle.quantize_rows(v[:, :-1])
+        kq = np.concatenate([kq, np.zeros((n, 1, D), np.int8)], axis=1)
+        vq = np.concatenate([vq, np.zeros((n, 1, D), np.int8)], axis=1)
+        ks = np.concatenate([ks, np.zeros((n, 1), np.float32)], axis=1)
+        vs = np.concatenate([vs, np.zeros((n, 1), np.float32)], axis=1)
+        chunks.append((k[:, -1].copy(), v[:, -1].copy(), q, kq, ks, vq, vs))
+    lens = np.full(n, L, np.int32)
+    done, t_work, steps = 0, 0.0, 0
+    while t_work < budget_s:
+        for knew, vnew, q, kq, ks, vq, vs in chunks:
+            t0 = time.perf_counter()
+            kq[:, -1], ks[:, -1] = oracle.quantize_rows(knew)
+            vq[:, -1], vs[:, -1] = oracle.quantize_rows(vnew)
+            for w in (0, 1024):
+                oracle.decode_ref(q, kq, ks, vq, vs, lens, w)
+            t_work += time.perf_counter() - t0
+            done += n
+        steps += 1
     info = threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     return {"value": done / t_work, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of the 64 sequences of one decode step (append + global layer + "
-                      f"window-1024 layer, 4096 keys, 32 heads, D=128); numpy float64 oracle, "
-                      f"{t_work:.1f} s of timed work",
+            "sample": f"{steps} decode steps of all 64 sequences (append + global layer + window-1024 layer, "
+                      f"4096 keys, 32 heads, D=128); numpy float64 oracle, {t_work:.1f} s of timed work",
             "host_cpus": len(os.sched_getaffinity(0)), "wall_s": time.perf_counter() - t_all}
 
 
