@@ -218,6 +218,10 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t vo
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
+// s_waitcnt immediate for "at most n vector memory operations outstanding"
+// (gfx9 encoding; expcnt and lgkmcnt left at no-wait).
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
 // Physical row of token position t of sequence b in a paged KV buffer:
 // block table[b][(t >> log2_bs) % table_len], entry clamped into the pool.
 __device__ __forceinline__ int64_t paged_row(const int32_t* table, int table_len, int log2_bs, int num_blocks,

@@ -25,9 +25,11 @@
 //    from LDS are free of bank conflicts; plus s_k * scale * log2(e) per key.
 //    E is a per-sequence power of two with 2^E >= max s_v (a small first
 //    pass), which keeps V'' in fp16's range; it is undone on the output.
-//  * Attention pass: work-group = 4 waves x 32 rows; staged tiles stream
-//    global -> LDS with direct-to-LDS loads (no registers), double-buffered,
-//    the next tile in flight while the current one is computed.
+//  * Attention pass: work-group = 8 waves x 32 rows, one per compute unit;
+//    staged tiles stream global -> LDS with direct-to-LDS loads (no
+//    registers) through three buffers, two tiles in flight while one is
+//    computed (with one tile ahead, the L2 round trip was exposed: 12% of the
+//    kernel); each wave waits only for its own copies of the next tile.
 //    S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (q and K exact in bf16);
 //    O^T += V''^T P^T on v_mfma_f32_16x16x32_f16 with P = 2^(z - m) in fp16
 //    (relative rounding 2^-11 on V'' and on P, inside the prefill
@@ -49,7 +51,8 @@ namespace {
 
 constexpr int kKeys = 64;        // keys per tile
 constexpr int kRowsPerWave = 32;
-constexpr int kWavesP = 4;
+constexpr int kWavesP = 8;
+constexpr int kStages = 3;
 constexpr int kRowsPerWG = kRowsPerWave * kWavesP;
 constexpr float kLazyP = 8.0f;
 
@@ -308,12 +311,18 @@ __device__ __forceinline__ void prefill_tile(const char* tl, const bf16x8 (&qop)
 // Attention pass.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_kernel(
+__global__ __launch_bounds__(64 * kWavesP) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_kernel(
     PrefillParams p) {
   constexpr int TB = StagedTile<D>::kBytes;
+  constexpr int NCH = TB / 1024;    // 1 KB copies per tile, spread over the waves
   constexpr int KK = D / 32;        // QK MFMAs along d
   constexpr int MT = D / 16;        // PV m-tiles
-  __shared__ __attribute__((aligned(16))) char lds[2][TB];
+  // Three separate buffers (not one indexed array), named statically in an
+  // unrolled loop, so the compiler can tell a buffer being read from the one
+  // being filled and does not wait for the copy in flight.
+  __shared__ __attribute__((aligned(16))) char lds0[TB];
+  __shared__ __attribute__((aligned(16))) char lds1[TB];
+  __shared__ __attribute__((aligned(16))) char lds2[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -353,14 +362,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const char* stage_b = p.stage + (int64_t)b * p.ntiles * TB;
 
   // Direct-to-LDS copy of staged tile t into buffer `buf`: 1 KB per
-  // instruction per wave; the 4 waves split the tile.
-  auto issue_tile = [&](int t, int buf) {
-    const char* src = stage_b + (int64_t)t * TB;
-    for (int ch = wave; ch < TB / 1024; ch += kWavesP)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + ch * 1024 + lane * 16),
-                                       reinterpret_cast<void*>(&lds[buf][ch * 1024]), 16, 0, 0);
+  // instruction per wave; the waves split the tile (wave w copies chunks
+  // w, w + kWavesP, ...: kLoadsHi copies for the first NCH % kWavesP waves,
+  // kLoadsLo for the others).
+  constexpr int kLoadsLo = NCH / kWavesP;
+  constexpr int kLoadsHi = kLoadsLo + (NCH % kWavesP != 0);
+  const bool more_loads = wave < NCH % kWavesP;
+  const __amdgpu_buffer_rsrc_t stage_r = make_rsrc(stage_b, (uint32_t)(p.ntiles * TB));
+  auto issue_tile = [&](int t, char* dst) {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(t * TB));
+#pragma unroll
+    for (int i = 0; i < kLoadsHi; ++i) {
+      const int ch = wave + i * kWavesP;
+      if (i < kLoadsLo || more_loads)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(stage_r, dst + ch * 1024, 16, (uint32_t)(ch * 1024 + lane * 16),
+                                                 soff, 0, 0);
+    }
   };
-  if (t0 < t1) issue_tile(t0, 0);
+  if (t0 < t1) issue_tile(t0, lds0);
+  if (t0 + 1 < t1) issue_tile(t0 + 1, lds1);
 
   const float E = p.seq_e[b];   // output scale 2^E undoes the V'' shift
 
@@ -396,11 +416,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = t0; t < t1; ++t) {
-    const int buf = (t - t0) & 1;
-    if (t + 1 < t1) issue_tile(t + 1, buf ^ 1);
+  // One tile: fill `fill` with tile t + 2 (its buffer was freed by the
+  // barrier that ended tile t - 1), compute tile t from `tl`, wait for tile
+  // t + 1, barrier.
+  auto step = [&](int t, const char* tl, char* fill) {
+    if (t + 2 < t1) issue_tile(t + 2, fill);
     const int base = t * kKeys;
-    const char* tl = lds[buf];
     if (wave_live && base < w_khi && base + kKeys > w_klo) {
       const bool need_mask = (base < w_klo) || (base + kKeys > P + w_r0 / Hq + 1) ||
                              (p.window > 0 && base < key_lo(P + (w_r1 - 1) / Hq));
@@ -409,8 +430,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       else
         prefill_tile<D, false>(tl, qop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g, c);
     }
-    __builtin_amdgcn_s_waitcnt(0);   // tile t+1 has landed in LDS
-    __syncthreads();                 // ... for every wave; buffer `buf` is free
+    // tile t+1 has landed in LDS (only tile t+2's copies may be in flight;
+    // this loop issues no other vector memory operations) ...
+    if (t + 2 < t1) {
+      if (more_loads)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsHi));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsLo));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();                 // ... for every wave; the buffer of tile t is free
+  };
+  for (int t = t0; t < t1; t += kStages) {
+    step(t, lds0, lds2);
+    if (t + 1 >= t1) break;
+    step(t + 1, lds1, lds0);
+    if (t + 2 >= t1) break;
+    step(t + 2, lds2, lds1);
   }
 
   // ---- normalise and write: lane holds out[row 16rt + c][16mt + 4g + 0..3] ----
@@ -473,10 +510,10 @@ int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& lay
   hipLaunchKernelGGL(prefill_exponent_kernel, dim3(B), dim3(256), 0, stream, prm);
   if (D == 128) {
     hipLaunchKernelGGL(prefill_stage_kernel<128>, sgrid, dim3(256), 0, stream, prm);
-    hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3((unsigned)grid), dim3(64 * kWavesP), 0, stream, prm);
   } else {
     hipLaunchKernelGGL(prefill_stage_kernel<64>, sgrid, dim3(256), 0, stream, prm);
-    hipLaunchKernelGGL(prefill_attn_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL(prefill_attn_kernel<64>, dim3((unsigned)grid), dim3(64 * kWavesP), 0, stream, prm);
   }
   return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
