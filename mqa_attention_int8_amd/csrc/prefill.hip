@@ -27,9 +27,11 @@
 //    pass), which keeps V'' in fp16's range; it is undone on the output.
 //  * Attention pass: work-group = 8 waves x 32 rows, one per compute unit;
 //    staged tiles stream global -> LDS with direct-to-LDS loads (no
-//    registers) through three buffers, two tiles in flight while one is
+//    registers) through four buffers, two tiles ahead of the one being
 //    computed (with one tile ahead, the L2 round trip was exposed: 12% of the
-//    kernel); each wave waits only for its own copies of the next tile.
+//    kernel); each wave waits only for its own copies of the next tile. The
+//    two waves of each SIMD run half a tile apart, and LDS operand reads are
+//    issued one MFMA block ahead.
 //    S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (q and K exact in bf16);
 //    O^T += V''^T P^T on v_mfma_f32_16x16x32_f16 with P = 2^(z - m) in fp16
 //    (relative rounding 2^-11 on V'' and on P, inside the prefill
@@ -52,11 +54,15 @@ namespace {
 constexpr int kKeys = 64;        // keys per tile
 constexpr int kRowsPerWave = 32;
 constexpr int kWavesP = 8;
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 constexpr int kRowsPerWG = kRowsPerWave * kWavesP;
 constexpr float kLazyP = 8.0f;
 
 // Staged tile: [K bf16 64 x D][V''^T fp16 D x 64][kscl 64 f32][pad to 1 KB]
+// K row `key` keeps its 16-byte chunk c at c ^ (key & kSwzK): one MFMA
+// operand read (16 keys x 4 chunks) then touches every LDS bank equally.
+template <int D>
+constexpr int kSwzK = D / 8 - 1;
 template <int D>
 struct StagedTile {
   static constexpr int kBytesK = kKeys * D * 2;
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
   char* tile = p.stage + ((int64_t)b * p.ntiles + t) * StagedTile<D>::kBytes;
 
   // K: thread = (key, quarter of the row); 16-byte chunk c of row `key` is
-  // stored at chunk c ^ (key & 7).
+  // stored at chunk c ^ (key & kSwzK).
   {
     constexpr int QB = D / 4;   // bytes of the row per thread (32 or 16)
     const int key = tid >> 2, qtr = tid & 3;
@@ -159,7 +165,7 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
       for (int h = 0; h < 2; ++h) {
         const int chunk = (qtr * QB) / 8 + 2 * u + h;   // 8 bf16 per chunk
         const u32x4 o = cat(i8x4_to_bf16(w[u][2 * h]), i8x4_to_bf16(w[u][2 * h + 1]));
-        *reinterpret_cast<u32x4*>(row + 8 * (chunk ^ (key & 7))) = o;
+        *reinterpret_cast<u32x4*>(row + 8 * (chunk ^ (key & kSwzK<D>))) = o;
       }
   }
   // V''^T: thread = (key group (ks, g), 4 columns). Chunk (ks, g) of row d
@@ -201,110 +207,154 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
   }
 }
 
-// One 64-key tile of one wave: S^T = K Q^T, online softmax, O^T += V''^T P^T.
-// MASK: the tile straddles a row's causal or window limit.
-template <int D, bool MASK>
-__device__ __forceinline__ void prefill_tile(const char* tl, const bf16x8 (&qop)[2][D / 32],
-                                             f32x4 (&oacc)[D / 16][2], f32x4 (&lacc)[2],
-                                             float (&m_run)[2], const f16x8& ones, int base,
-                                             const int (&row_lo)[2], const int (&row_pos)[2], int g,
-                                             int c) {
-  constexpr int KK = D / 32;
-  constexpr int MT = D / 16;
-  // ---- S^T = K Q^T ----
-  f32x4 s[4][2];
+// One 64-key tile of one wave in three parts: S^T = K Q^T (tile_qk), the
+// online softmax of one 16-row block (tile_softmax, once per block), and
+// O^T += V''^T P^T (tile_pv). Split so that a wave can run the parts of
+// consecutive tiles in a rotated order (see the attention pass).
+// Scales s_k * scale * log2(e) of this lane's keys 16kb + 4g + r.
+template <int D>
+__device__ __forceinline__ void load_kscl(const char* tl, f32x4 (&kscl)[4], int g) {
+  const float* scl = reinterpret_cast<const float*>(tl + StagedTile<D>::kOffScl);
 #pragma unroll
-  for (int kb4 = 0; kb4 < 4; ++kb4) {
-    s[kb4][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    s[kb4][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb4 = 0; kb4 < 4; ++kb4) kscl[kb4] = *reinterpret_cast<const f32x4*>(scl + 16 * kb4 + 4 * g);
+}
+
+// The K operand reads of each 16-key block are issued one block ahead of
+// its MFMAs (scheduling barriers keep that order), so the LDS latency hides
+// behind the previous block's MFMAs.
+template <int D>
+__device__ __forceinline__ void tile_qk(const char* tl, const bf16x8 (&qop)[2][D / 32], f32x4 (&s)[4][2], int g,
+                                        int c) {
+  constexpr int KK = D / 32;
+  u32x4 kc[4][KK];
+  const auto read = [&](int kb4) {
     const int key = 16 * kb4 + c;
     const uint16_t* krow = reinterpret_cast<const uint16_t*>(tl) + key * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int chunk = (4 * kk + g) ^ (key & 7);
-      const bf16x8 kop = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 8 * chunk));
+      const int chunk = (4 * kk + g) ^ (key & kSwzK<D>);
+      kc[kb4][kk] = *reinterpret_cast<const u32x4*>(krow + 8 * chunk);
+    }
+  };
+  read(0);
+#pragma unroll
+  for (int kb4 = 0; kb4 < 4; ++kb4) {
+    if (kb4 + 1 < 4) read(kb4 + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    s[kb4][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s[kb4][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 kop = as_bf16x8(kc[kb4][kk]);
       s[kb4][0] = mfma16(kop, qop[0][kk], s[kb4][0]);
       s[kb4][1] = mfma16(kop, qop[1][kk], s[kb4][1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // ---- scales of this lane's keys 16kb + 4g + r ----
-  const float* scl = reinterpret_cast<const float*>(tl + StagedTile<D>::kOffScl);
+}
+
+// Online softmax of row block RT (rows 16RT + c of the wave) over one tile:
+// t = s * kscl - m, weight 2^t as fp16 P (two 32-key halves), row sums by
+// an MFMA against an all-ones block. MASK: the tile straddles a row's causal
+// or window limit.
+template <int D, bool MASK, int RT>
+__device__ __forceinline__ void tile_softmax(const char* tl, const f32x4 (&s)[4][2], f16x8 (&pop)[2][2],
+                                             f32x4 (&oacc)[D / 16][2], f32x4 (&lacc)[2], float (&m_run)[2],
+                                             const f16x8& ones, int base, const int (&row_lo)[2],
+                                             const int (&row_pos)[2], int g) {
+  constexpr int MT = D / 16;
   f32x4 kscl[4];
+  load_kscl<D>(tl, kscl, g);
+  float tz[16];
 #pragma unroll
-  for (int kb4 = 0; kb4 < 4; ++kb4) kscl[kb4] = *reinterpret_cast<const f32x4*>(scl + 16 * kb4 + 4 * g);
-  // ---- online softmax per row: t = s * kscl - m_run, weight 2^t ----
-  f16x8 pop[2][2];  // [row block][32-key step]
+  for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    float tz[16];
+    for (int r = 0; r < 4; ++r) tz[4 * kb4 + r] = fmaf(s[kb4][RT][r], kscl[kb4][r], -m_run[RT]);
+  if constexpr (MASK) {   // boundary tiles only
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = base + 16 * (i >> 2) + 4 * g + (i & 3);
+      tz[i] = (j >= row_lo[RT] && j <= row_pos[RT]) ? tz[i] : -INFINITY;
+    }
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, tz[i]);
+  tmax = quad_max(tmax);
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > kLazyP) != 0, 0)) {
+    // Rare: move the running max to this tile's max and rescale.
+    // (m_run = -inf makes every visible t = +inf; recompute from s.)
+    float zmax = -INFINITY;
 #pragma unroll
     for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tz[4 * kb4 + r] = fmaf(s[kb4][rt][r], kscl[kb4][r], -m_run[rt]);
-    if constexpr (MASK) {   // boundary tiles only
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = base + 16 * (i >> 2) + 4 * g + (i & 3);
-        tz[i] = (j >= row_lo[rt] && j <= row_pos[rt]) ? tz[i] : -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * kb4 + r;
+        const float z = s[kb4][RT][r] * kscl[kb4][r];
+        tz[i] = (tz[i] == -INFINITY) ? -INFINITY : z;   // keep the mask
+        zmax = fmaxf(zmax, tz[i]);
       }
-    }
-    float tmax = -INFINITY;
+    zmax = quad_max(zmax);
+    const float m_new = fmaxf(m_run[RT], zmax);
+    // rows of the wave may differ in position: a row with no visible key
+    // yet keeps m = -inf and must not form 2^(-inf - -inf)
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[RT] - m_new);
+    m_run[RT] = m_new;
+    lacc[RT] *= alpha;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, tz[i]);
-    tmax = quad_max(tmax);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(tmax > kLazyP) != 0, 0)) {
-      // Rare: move the running max to this tile's max and rescale.
-      // (m_run = -inf makes every visible t = +inf; recompute from s.)
-      float zmax = -INFINITY;
+    for (int mt = 0; mt < MT; ++mt) oacc[mt][RT] *= alpha;
+    const float msub = (m_new == -INFINITY) ? 0.f : m_new;
 #pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * kb4 + r;
-          const float z = s[kb4][rt][r] * kscl[kb4][r];
-          tz[i] = (tz[i] == -INFINITY) ? -INFINITY : z;   // keep the mask
-          zmax = fmaxf(zmax, tz[i]);
-        }
-      zmax = quad_max(zmax);
-      const float m_new = fmaxf(m_run[rt], zmax);
-      // rows of the wave may differ in position: a row with no visible key
-      // yet keeps m = -inf and must not form 2^(-inf - -inf)
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[rt] - m_new);
-      m_run[rt] = m_new;
-      lacc[rt] *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) oacc[mt][rt] *= alpha;
-      const float msub = (m_new == -INFINITY) ? 0.f : m_new;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tz[i] -= msub;
-    }
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      u32x4 w;
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const int zi = 8 * ks2 + i;
-        w[i >> 1] = cvt_pk_f16(fast_exp2(tz[zi]), fast_exp2(tz[zi + 1]));
-      }
-      pop[rt][ks2] = __builtin_bit_cast(f16x8, w);
-      lacc[rt] = mfma16_f16(ones, pop[rt][ks2], lacc[rt]);
-    }
+    for (int i = 0; i < 16; ++i) tz[i] -= msub;
   }
-  // ---- O^T += V''^T P^T (fp16) ----
-  const uint16_t* vt = reinterpret_cast<const uint16_t*>(tl + StagedTile<D>::kBytesK);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const int zi = 8 * ks2 + i;
+      w[i >> 1] = cvt_pk_f16(fast_exp2(tz[zi]), fast_exp2(tz[zi + 1]));
+    }
+    pop[RT][ks2] = __builtin_bit_cast(f16x8, w);
+    lacc[RT] = mfma16_f16(ones, pop[RT][ks2], lacc[RT]);
+  }
+}
+
+// As in tile_qk, the V operand reads of each pair of 16-column blocks are
+// issued one pair ahead of their MFMAs.
+template <int D>
+__device__ __forceinline__ void tile_pv(const char* tl, const f16x8 (&pop)[2][2], f32x4 (&oacc)[D / 16][2], int g,
+                                        int c) {
+  constexpr int MT = D / 16;
+  const uint16_t* vt = reinterpret_cast<const uint16_t*>(tl + StagedTile<D>::kBytesK);
+  u32x4 vc[MT][2];
+  const auto read = [&](int mt) {
     const int d = 16 * mt + c;
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       const int chunk = (4 * ks2 + g) ^ (d & 7);
-      const f16x8 vop =
-          __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(vt + d * kKeys + 8 * chunk));
-      oacc[mt][0] = mfma16_f16(vop, pop[0][ks2], oacc[mt][0]);
-      oacc[mt][1] = mfma16_f16(vop, pop[1][ks2], oacc[mt][1]);
+      vc[mt][ks2] = *reinterpret_cast<const u32x4*>(vt + d * kKeys + 8 * chunk);
     }
+  };
+  read(0);
+  read(1);
+#pragma unroll
+  for (int mp = 0; mp < MT; mp += 2) {
+    if (mp + 2 < MT) {
+      read(mp + 2);
+      read(mp + 3);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = mp; mt < mp + 2; ++mt)
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const f16x8 vop = __builtin_bit_cast(f16x8, vc[mt][ks2]);
+        oacc[mt][0] = mfma16_f16(vop, pop[0][ks2], oacc[mt][0]);
+        oacc[mt][1] = mfma16_f16(vop, pop[1][ks2], oacc[mt][1]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
   }
-
 }
 
 // ---------------------------------------------------------------------------
@@ -317,12 +367,13 @@ __global__ __launch_bounds__(64 * kWavesP) __attribute__((amdgpu_waves_per_eu(2)
   constexpr int NCH = TB / 1024;    // 1 KB copies per tile, spread over the waves
   constexpr int KK = D / 32;        // QK MFMAs along d
   constexpr int MT = D / 16;        // PV m-tiles
-  // Three separate buffers (not one indexed array), named statically in an
+  // Four separate buffers (not one indexed array), named statically in an
   // unrolled loop, so the compiler can tell a buffer being read from the one
   // being filled and does not wait for the copy in flight.
   __shared__ __attribute__((aligned(16))) char lds0[TB];
   __shared__ __attribute__((aligned(16))) char lds1[TB];
   __shared__ __attribute__((aligned(16))) char lds2[TB];
+  __shared__ __attribute__((aligned(16))) char lds3[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -416,23 +467,21 @@ __global__ __launch_bounds__(64 * kWavesP) __attribute__((amdgpu_waves_per_eu(2)
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // One tile: fill `fill` with tile t + 2 (its buffer was freed by the
-  // barrier that ended tile t - 1), compute tile t from `tl`, wait for tile
-  // t + 1, barrier.
-  auto step = [&](int t, const char* tl, char* fill) {
-    if (t + 2 < t1) issue_tile(t + 2, fill);
-    const int base = t * kKeys;
-    if (wave_live && base < w_khi && base + kKeys > w_klo) {
-      const bool need_mask = (base < w_klo) || (base + kKeys > P + w_r0 / Hq + 1) ||
-                             (p.window > 0 && base < key_lo(P + (w_r1 - 1) / Hq));
-      if (need_mask)
-        prefill_tile<D, true>(tl, qop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g, c);
-      else
-        prefill_tile<D, false>(tl, qop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g, c);
-    }
-    // tile t+1 has landed in LDS (only tile t+2's copies may be in flight;
-    // this loop issues no other vector memory operations) ...
-    if (t + 2 < t1) {
+
+  // Tile steps, each in two halves with a barrier after each: half 1 = issue
+  // the copies of tile t + 2, QK and the softmax of row block 0; half 2 = the
+  // softmax of row block 1 and PV. Waves 4-7 (one per SIMD beside waves 0-3)
+  // pass one extra barrier first and so run half a step behind: while one
+  // wave of a SIMD issues MFMAs the other runs its softmax on the vector
+  // ALUs. Between two barriers the waves read tiles t - 1 and t (tile t from
+  // the first barrier before its QK to the third after), so tile t + 2 goes
+  // into the buffer of tile t - 2, of four. Before each barrier a wave waits
+  // for its own copies of tile t + 1, which the half-step-late waves need
+  // landed one barrier earlier than the others do.
+  const bool late = wave >= kWavesP / 2;
+  if (late && t0 < t1) __syncthreads();
+  const auto wait_next = [&](int t) {
+    if (t + 2 < t1) {   // only tile t+2's copies may still be in flight
       if (more_loads)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsHi));
       else
@@ -440,14 +489,44 @@ __global__ __launch_bounds__(64 * kWavesP) __attribute__((amdgpu_waves_per_eu(2)
     } else {
       __builtin_amdgcn_s_waitcnt(0);
     }
-    __syncthreads();                 // ... for every wave; the buffer of tile t is free
+  };
+  f32x4 s[4][2];
+  f16x8 pop[2][2];
+  const auto step = [&](int t, const char* tl, char* fill) {
+    if (t + 2 < t1) issue_tile(t + 2, fill);
+    const int base = t * kKeys;
+    const bool live = wave_live && base < w_khi && base + kKeys > w_klo;
+    const bool masked = (base < w_klo) || (base + kKeys > P + w_r0 / Hq + 1) ||
+                        (p.window > 0 && base < key_lo(P + (w_r1 - 1) / Hq));
+    if (live) {
+      tile_qk<D>(tl, qop, s, g, c);
+      if (masked)
+        tile_softmax<D, true, 0>(tl, s, pop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g);
+      else
+        tile_softmax<D, false, 0>(tl, s, pop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g);
+    }
+    wait_next(t);
+    __syncthreads();
+    if (live) {
+      if (masked)
+        tile_softmax<D, true, 1>(tl, s, pop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g);
+      else
+        tile_softmax<D, false, 1>(tl, s, pop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g);
+      tile_pv<D>(tl, pop, oacc, g, c);
+    }
+    if (!(late && t + 1 == t1)) {   // the late waves passed their extra barrier first
+      wait_next(t);
+      __syncthreads();
+    }
   };
   for (int t = t0; t < t1; t += kStages) {
     step(t, lds0, lds2);
     if (t + 1 >= t1) break;
-    step(t + 1, lds1, lds0);
+    step(t + 1, lds1, lds3);
     if (t + 2 >= t1) break;
-    step(t + 2, lds2, lds1);
+    step(t + 2, lds2, lds0);
+    if (t + 3 >= t1) break;
+    step(t + 3, lds3, lds1);
   }
 
   // ---- normalise and write: lane holds out[row 16rt + c][16mt + 4g + 0..3] ----
