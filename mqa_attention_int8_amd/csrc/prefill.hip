@@ -111,22 +111,37 @@ __device__ __forceinline__ int first_needed_key(int P, int window) {
 }
 
 // ---------------------------------------------------------------------------
-// Exponent pass: grid (B), 256 threads. E = smallest e with 2^e >= max s_v
-// over the keys the chunk can see.
+// Exponent pass: grid (B), kExpThreads threads. E = smallest e with
+// 2^e >= max s_v over the keys the chunk can see. Each thread keeps four
+// loads in flight (one load per thread at a time left the pass bound by
+// dozens of dependent memory round trips).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void prefill_exponent_kernel(PrefillParams p) {
+constexpr int kExpThreads = 1024;
+constexpr int kExpUnroll = 4;
+__global__ __launch_bounds__(kExpThreads) void prefill_exponent_kernel(PrefillParams p) {
   const int b = blockIdx.x, tid = threadIdx.x;
-  __shared__ float red[4];
+  __shared__ float red[kExpThreads / kWave];
   const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.P_max);
   const int lo = first_needed_key(P, p.window), hi = P + p.C;
   float m = 0.f;
-  for (int j = lo + tid; j < hi; j += 256) m = fmaxf(m, fabsf(p.vs[key_row(p, b, j)]));
+  for (int j0 = lo + tid; j0 < hi; j0 += kExpUnroll * kExpThreads) {
+    float v[kExpUnroll];
+#pragma unroll
+    for (int u = 0; u < kExpUnroll; ++u) {
+      const int j = j0 + u * kExpThreads;
+      v[u] = j < hi ? fabsf(p.vs[key_row(p, b, j)]) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kExpUnroll; ++u) m = fmaxf(m, v[u]);
+  }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, kWave));
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   if (tid == 0) {
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    m = 0.f;
+#pragma unroll
+    for (int w = 0; w < kExpThreads / kWave; ++w) m = fmaxf(m, red[w]);
     int e = 0;
     if (m > 0.f && m < INFINITY) (void)frexpf(m, &e);
     p.seq_e[b] = (float)e;
@@ -586,7 +601,7 @@ int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& lay
   const int64_t grid = (int64_t)prm.row_tiles * B;
   if (grid > 0x7fffffff) return MQA_ERR_SHAPE;
   const dim3 sgrid(prm.ntiles, B);
-  hipLaunchKernelGGL(prefill_exponent_kernel, dim3(B), dim3(256), 0, stream, prm);
+  hipLaunchKernelGGL(prefill_exponent_kernel, dim3(B), dim3(kExpThreads), 0, stream, prm);
   if (D == 128) {
     hipLaunchKernelGGL(prefill_stage_kernel<128>, sgrid, dim3(256), 0, stream, prm);
     hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3((unsigned)grid), dim3(64 * kWavesP), 0, stream, prm);
