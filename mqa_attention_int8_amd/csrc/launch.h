@@ -28,6 +28,7 @@ struct DecodePlan {
   int tiles_per_part;  // 32-key tiles per work-group
   int num_parts;       // work-groups per sequence
   size_t ws_bytes;     // workspace for partial states (0 when num_parts == 1)
+  int heads_per_group; // query heads per work-group (grid z = ceil(Hq / heads_per_group))
 };
 // block_size > 0: paged layout (bounds the tiles of a partition).
 DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,
