@@ -270,13 +270,16 @@ __device__ __forceinline__ void tile_qk(const char* tl, const bf16x8 (&qop)[2][D
 
 // Online softmax of row block RT (rows 16RT + c of the wave) over one tile:
 // t = s * kscl - m, weight 2^t as fp16 P (two 32-key halves), row sums by
-// an MFMA against an all-ones block. MASK: the tile straddles a row's causal
-// or window limit.
-template <int D, bool MASK, int RT>
+// an MFMA against an all-ones block. `masked`: the tile straddles a row's
+// causal or window limit. One body for both cases (a runtime branch that
+// only rewrites the logits): with a separate masked copy, the joins of the
+// two copies and their rare rescale paths cost ~24 register-pair moves of
+// the accumulators per row block and tile on the common path.
+template <int D, int RT>
 __device__ __forceinline__ void tile_softmax(const char* tl, const f32x4 (&s)[4][2], f16x8 (&pop)[2][2],
                                              f32x4 (&oacc)[D / 16][2], f32x4 (&lacc)[2], float (&m_run)[2],
                                              const f16x8& ones, int base, const int (&row_lo)[2],
-                                             const int (&row_pos)[2], int g) {
+                                             const int (&row_pos)[2], int g, bool masked) {
   constexpr int MT = D / 16;
   f32x4 kscl[4];
   load_kscl<D>(tl, kscl, g);
@@ -285,7 +288,8 @@ __device__ __forceinline__ void tile_softmax(const char* tl, const f32x4 (&s)[4]
   for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
     for (int r = 0; r < 4; ++r) tz[4 * kb4 + r] = fmaf(s[kb4][RT][r], kscl[kb4][r], -m_run[RT]);
-  if constexpr (MASK) {   // boundary tiles only
+  if (masked) {   // boundary tiles only (wave-uniform; only the logits change)
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = base + 16 * (i >> 2) + 4 * g + (i & 3);
@@ -515,18 +519,12 @@ __global__ __launch_bounds__(64 * kWavesP) __attribute__((amdgpu_waves_per_eu(2)
                         (p.window > 0 && base < key_lo(P + (w_r1 - 1) / Hq));
     if (live) {
       tile_qk<D>(tl, qop, s, g, c);
-      if (masked)
-        tile_softmax<D, true, 0>(tl, s, pop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g);
-      else
-        tile_softmax<D, false, 0>(tl, s, pop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g);
+      tile_softmax<D, 0>(tl, s, pop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g, masked);
     }
     wait_next(t);
     __syncthreads();
     if (live) {
-      if (masked)
-        tile_softmax<D, true, 1>(tl, s, pop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g);
-      else
-        tile_softmax<D, false, 1>(tl, s, pop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g);
+      tile_softmax<D, 1>(tl, s, pop, oacc, lacc, m_run, ones, base, row_lo, row_pos, g, masked);
       tile_pv<D>(tl, pop, oacc, g, c);
     }
     if (!(late && t + 1 == t1)) {   // the late waves passed their extra barrier first
