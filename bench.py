@@ -84,8 +84,9 @@ def make_decode_buffers(torch, m, B, L, D, copies, gen):
     return bufs
 
 
-def run_steps(torch, fn, steps, use_graph, stream):
-    """Replay `fn` (which runs `period` steps) steps/period times; returns ms."""
+def run_steps(torch, fn, steps, use_graph, stream, warm=1):
+    """Replay `fn` (which runs `period` steps) steps/period times after `warm`
+    untimed replays; returns ms."""
     timer = Timer(torch, stream)
     if use_graph:
         g = torch.cuda.CUDAGraph()
@@ -93,7 +94,8 @@ def run_steps(torch, fn, steps, use_graph, stream):
             fn()
         torch.cuda.synchronize()
         reps = steps
-        g.replay()
+        for _ in range(max(1, warm)):
+            g.replay()
         torch.cuda.synchronize()
         timer.start()
         for _ in range(reps):
@@ -436,8 +438,10 @@ def bench_prefill(torch, m, acct, stream):
                 m.mqa_prefill_chunk(q, kv, plens, P, win, out=out, workspace=ws)
             call()
             torch.cuda.synchronize()
+            # untimed replays first: the first tens of ms of a long MFMA-bound
+            # kernel run slower than the settled rate (about 10% here)
             reps = 10
-            ms, _ = run_steps(torch, call, reps, True, stream)
+            ms, _ = run_steps(torch, call, reps, True, stream, warm=30 if win == 0 else 100)
             ms_call = ms / reps
             fl = acct.prefill_flops([P] * B, C, win, Hq, D)
             tf = fl / (ms_call * 1e-3) / 1e12
