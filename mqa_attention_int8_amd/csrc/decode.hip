@@ -46,6 +46,8 @@
 //    sequence's last row first encodes the new token's K and V into it.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -754,31 +756,41 @@ void decode_partition_kernel(DecodeParams p) {
 // Log-sum-exp merge of the partition states of one sequence and a group of
 // heads, o_p normalised: m = max_p m_p; w_p = l_p 2^(m_p - m);
 // out = sum_p w_p o_p / sum_p w_p.
-// Block = 256 threads = 8 heads x 32 float4 columns (D = 128) or 16 heads x
-// 16 columns (D = 64).
+// 256 threads = 8 heads x 32 float4 columns (D = 128) or 16 heads x 16
+// columns (D = 64), times S partition slices (block = 256 S threads, S <= 4):
+// slice s merges partitions s, s + S, ... with eight loads in flight at a
+// time and a running rescale, then slice 0 combines the S slices through LDS.
+// A long context (tens of partitions per sequence) thus needs one or two
+// dependent memory round trips instead of one per eight partitions.
+constexpr int kMergeMaxSlices = 4;
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ ws_o,
-                                                           const float2* __restrict__ ws_ml,
-                                                           float* __restrict__ out, int Hq, int P) {
+__global__ __launch_bounds__(256 * kMergeMaxSlices) void decode_merge_kernel(const float* __restrict__ ws_o,
+                                                                             const float2* __restrict__ ws_ml,
+                                                                             float* __restrict__ out, int Hq, int P) {
   constexpr int D4 = D / 4;
   constexpr int HPB = 256 / D4;  // heads per block
+  __shared__ f32x4 s_acc[kMergeMaxSlices - 1][256];
+  __shared__ float2 s_ml[kMergeMaxSlices - 1][256];
+  const int S = blockDim.x / 256;
+  const int slice = threadIdx.x / 256;
+  const int t = threadIdx.x % 256;
   const int b = blockIdx.y;
-  const int h = blockIdx.x * HPB + threadIdx.x / D4;
-  const int d0 = 4 * (threadIdx.x % D4);
-  if (h >= Hq) return;
+  const int h = blockIdx.x * HPB + t / D4;
+  const int d0 = 4 * (t % D4);
+  const bool live_h = h < Hq;
   const float2* ml = ws_ml + (int64_t)b * P * Hq + h;
   const float* wo = ws_o + ((int64_t)b * P * Hq + h) * D + d0;
-  // One pass, eight partitions' loads in flight at a time, running rescale.
   float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int q0 = 0; q0 < P; q0 += 8) {
+  for (int q0 = slice; q0 < P; q0 += 8 * S) {
     float2 st[8];
     f32x4 o[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const bool live = q0 + u < P;
-      st[u] = live ? ml[(int64_t)(q0 + u) * Hq] : make_float2(-INFINITY, 0.f);
-      o[u] = live ? *reinterpret_cast<const f32x4*>(wo + (int64_t)(q0 + u) * Hq * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const int pp = q0 + u * S;
+      const bool live = live_h && pp < P;
+      st[u] = live ? ml[(int64_t)pp * Hq] : make_float2(-INFINITY, 0.f);
+      o[u] = live ? *reinterpret_cast<const f32x4*>(wo + (int64_t)pp * Hq * D) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float Mc = M;
 #pragma unroll
@@ -795,6 +807,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     }
     M = Mc;
   }
+  if (S > 1) {
+    if (slice > 0) {
+      s_acc[slice - 1][t] = acc;
+      s_ml[slice - 1][t] = make_float2(M, L);
+    }
+    __syncthreads();
+    if (slice > 0) return;
+    for (int j = 0; j < S - 1; ++j) {
+      const float2 x = s_ml[j][t];
+      const float Mc = fmaxf(M, x.x);
+      if (Mc == -INFINITY) continue;
+      const float a = exp2f(M - Mc), w = exp2f(x.x - Mc);
+      acc = acc * a + s_acc[j][t] * w;
+      L = L * a + x.y * w;
+      M = Mc;
+    }
+  }
+  if (!live_h) return;
   const float inv = L > 0.f ? 1.f / L : 0.f;
   *reinterpret_cast<f32x4*>(out + ((int64_t)b * Hq + h) * D + d0) = acc * inv;
 }
@@ -914,11 +944,13 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layo
   if (plan.num_parts > 1) {
     const int hpb = 256 / (D / 4);
     const dim3 grid((Hq + hpb - 1) / hpb, B);
+    const int slices = std::min(kMergeMaxSlices, (plan.num_parts + 7) / 8);
+    const dim3 block(256 * slices);
     if (D == 128)
-      hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(256), 0, stream, prm.ws_o, prm.ws_ml, out, Hq,
+      hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, stream, prm.ws_o, prm.ws_ml, out, Hq,
                          plan.num_parts);
     else
-      hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(256), 0, stream, prm.ws_o, prm.ws_ml, out, Hq,
+      hipLaunchKernelGGL(decode_merge_kernel<64>, grid, block, 0, stream, prm.ws_o, prm.ws_ml, out, Hq,
                          plan.num_parts);
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
   }
