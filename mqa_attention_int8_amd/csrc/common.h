@@ -205,6 +205,18 @@ __device__ __forceinline__ float quad_sum(float v) {
 // below the normal range flush to 0, which only drops negligible weights).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A pointer every lane holds alike, moved to scalar registers. A buffer
+// resource built from a value the compiler keeps in vector registers (it
+// does so under scalar register pressure) is re-made in every load by a
+// loop over the distinct values of the wave.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Buffer resource over [base, base + bytes): loads beyond it return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);

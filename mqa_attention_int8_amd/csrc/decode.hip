@@ -550,7 +550,8 @@ void decode_partition_kernel(DecodeParams p) {
   u32x4 qraw[NT][KK];
   QOperand<D, NT, Q8> qop;
   if constexpr (!Q8) {
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q + ((int64_t)b * Hq + h0) * D, (uint32_t)(Hg * D * 2));
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(uniform_ptr(p.q + ((int64_t)b * Hq + h0) * D),
+                                                __builtin_amdgcn_readfirstlane((uint32_t)(Hg * D * 2)));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -559,8 +560,10 @@ void decode_partition_kernel(DecodeParams p) {
   } else {
     // lane (g, c): bytes g*D/4 + 16w .. +15 of row 16nt + c, the same
     // contraction indices as the K bytes it holds
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q8 + ((int64_t)b * Hq + h0) * D, (uint32_t)(Hg * D));
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.q_scale + (int64_t)b * Hq + h0, (uint32_t)(Hg * 4));
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(uniform_ptr(p.q8 + ((int64_t)b * Hq + h0) * D),
+                                                __builtin_amdgcn_readfirstlane((uint32_t)(Hg * D)));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(uniform_ptr(p.q_scale + (int64_t)b * Hq + h0),
+                                                __builtin_amdgcn_readfirstlane((uint32_t)(Hg * 4)));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
