@@ -13,7 +13,9 @@
 //  * One work-group = one sequence x one contiguous range of 32-key tiles
 //    (a "partition") x up to 32 query heads (more heads: more head groups
 //    in grid z). Each K/V byte is read from HBM once per call and head group
-//    and feeds all its heads: this is where MQA's reuse lives.
+//    and feeds all its heads: this is where MQA's reuse lives. Short visible
+//    ranges (sliding windows) instead run 16-head groups over the whole
+//    range, with no partitions to merge (plan_decode).
 //  * Eight waves per work-group, one work-group per compute unit. The
 //    work-group's tiles are handed to its waves from an LDS counter, so the
 //    waves finish together whatever the SIMD arbiter favours (which wave sums
