@@ -1,0 +1,38 @@
+"""Host-side checks of bench.py's contract (no GPU).
+
+Only one GPU is measured: asking for more must fail with a message before
+any device work. The HBM-traffic figure reported beside the roofline must
+come from a counter record whose source hash matches the decode sources.
+"""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_counted_traffic_follows_the_sources(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    rec = json.load(open(os.path.join(ROOT, "profiles", "decode_global_traffic.json")))
+    # the committed record matches the committed sources
+    assert bench.counted_traffic() == rec["traffic_bytes_per_launch"]
+    # a record taken on other sources is not reported
+    fake = tmp_path / "repo"
+    (fake / "profiles").mkdir(parents=True)
+    for f in rec["source_files"]:
+        dst = fake / f
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        dst.write_bytes(open(os.path.join(ROOT, f), "rb").read() + b"\n// changed\n")
+    (fake / "profiles" / "decode_global_traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench.os.path, "abspath", lambda p: str(fake / "bench.py"))
+    assert bench.counted_traffic() is None
