@@ -148,10 +148,20 @@ __global__ __launch_bounds__(kExpThreads) void prefill_exponent_kernel(PrefillPa
   }
 }
 
+// Row of key j of sequence b, with the layout fixed at compile time.
+template <bool PAGED>
+__device__ __forceinline__ int64_t key_row_of(const PrefillParams& p, int b, int j) {
+  if constexpr (!PAGED) return (int64_t)b * p.L_cap + j;
+  else return paged_row(p.table, p.table_len, p.log2_bs, p.num_blocks, b, j);
+}
+
 // ---------------------------------------------------------------------------
 // Stage pass: grid (ntiles, B), 256 threads, one 64-key tile per work-group.
+// Keys past the last one (kend) are read at row kend - 1 and zeroed after the
+// load, so every load of a thread is issued before the first wait (loads
+// under per-key conditions each waited for the previous one).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
   const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.P_max);
@@ -168,11 +178,13 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
     constexpr int QB = D / 4;   // bytes of the row per thread (32 or 16)
     const int key = tid >> 2, qtr = tid & 3;
     const int j = base + key;
+    const bool ok = j < kend;
+    const int64_t krow = key_row_of<PAGED>(p, b, ok ? j : kend - 1);
     u32x4 w[QB / 16];
 #pragma unroll
-    for (int u = 0; u < QB / 16; ++u)
-      w[u] = j < kend ? *reinterpret_cast<const u32x4*>(p.k + key_row(p, b, j) * D + qtr * QB + 16 * u)
-                      : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < QB / 16; ++u) w[u] = *reinterpret_cast<const u32x4*>(p.k + krow * D + qtr * QB + 16 * u);
+#pragma unroll
+    for (int u = 0; u < QB / 16; ++u) w[u] = ok ? w[u] : u32x4{0u, 0u, 0u, 0u};
     uint16_t* row = reinterpret_cast<uint16_t*>(tile) + key * D;
 #pragma unroll
     for (int u = 0; u < QB / 16; ++u)
@@ -194,13 +206,23 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
       const int ks = grp >> 2, g = grp & 3;
       uint32_t w[8];
       float f[8];
+      int64_t row[8];
+      bool ok[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int j = base + 32 * ks + 16 * (i >> 2) + 4 * g + (i & 3);
-        const bool ok = j < kend;
-        const int64_t row = ok ? key_row(p, b, j) : 0;
-        w[i] = ok ? *reinterpret_cast<const uint32_t*>(p.v + row * D + 4 * dq) : 0u;
-        f[i] = ok ? p.vs[row] * rE : 0.f;   // exact: a power-of-two rescale
+        ok[i] = j < kend;
+        row[i] = key_row_of<PAGED>(p, b, ok[i] ? j : kend - 1);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w[i] = *reinterpret_cast<const uint32_t*>(p.v + row[i] * D + 4 * dq);
+        f[i] = p.vs[row[i]];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w[i] = ok[i] ? w[i] : 0u;
+        f[i] = ok[i] ? f[i] * rE : 0.f;   // exact: a power-of-two rescale
       }
       uint16_t* vt = reinterpret_cast<uint16_t*>(tile + StagedTile<D>::kBytesK);
 #pragma unroll
@@ -217,7 +239,8 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
   // Per-key s_k * scale * log2(e).
   if (tid < kKeys) {
     const int j = base + tid;
-    const float sk = j < kend ? p.ks[key_row(p, b, j)] * p.scale_log2 : 0.f;
+    const float skr = p.ks[key_row_of<PAGED>(p, b, j < kend ? j : kend - 1)];
+    const float sk = j < kend ? skr * p.scale_log2 : 0.f;
     reinterpret_cast<float*>(tile + StagedTile<D>::kOffScl)[tid] = sk;
   }
 }
@@ -601,10 +624,16 @@ int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& lay
   const dim3 sgrid(prm.ntiles, B);
   hipLaunchKernelGGL(prefill_exponent_kernel, dim3(B), dim3(kExpThreads), 0, stream, prm);
   if (D == 128) {
-    hipLaunchKernelGGL(prefill_stage_kernel<128>, sgrid, dim3(256), 0, stream, prm);
+    if (prm.table)
+      hipLaunchKernelGGL((prefill_stage_kernel<128, true>), sgrid, dim3(256), 0, stream, prm);
+    else
+      hipLaunchKernelGGL((prefill_stage_kernel<128, false>), sgrid, dim3(256), 0, stream, prm);
     hipLaunchKernelGGL(prefill_attn_kernel<128>, dim3((unsigned)grid), dim3(64 * kWavesP), 0, stream, prm);
   } else {
-    hipLaunchKernelGGL(prefill_stage_kernel<64>, sgrid, dim3(256), 0, stream, prm);
+    if (prm.table)
+      hipLaunchKernelGGL((prefill_stage_kernel<64, true>), sgrid, dim3(256), 0, stream, prm);
+    else
+      hipLaunchKernelGGL((prefill_stage_kernel<64, false>), sgrid, dim3(256), 0, stream, prm);
     hipLaunchKernelGGL(prefill_attn_kernel<64>, dim3((unsigned)grid), dim3(64 * kWavesP), 0, stream, prm);
   }
   return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
