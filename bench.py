@@ -438,10 +438,11 @@ def bench_prefill(torch, m, acct, stream):
                 m.mqa_prefill_chunk(q, kv, plens, P, win, out=out, workspace=ws)
             call()
             torch.cuda.synchronize()
-            # untimed replays first: the first tens of ms of a long MFMA-bound
-            # kernel run slower than the settled rate (about 10% here)
+            # untimed replays first (~0.1 s): the first ~50 ms of back-to-back
+            # calls of this MFMA-bound kernel run up to ~15% slower than the
+            # settled rate
             reps = 10
-            ms, _ = run_steps(torch, call, reps, True, stream, warm=30 if win == 0 else 100)
+            ms, _ = run_steps(torch, call, reps, True, stream, warm=80 if win == 0 else 200)
             ms_call = ms / reps
             fl = acct.prefill_flops([P] * B, C, win, Hq, D)
             tf = fl / (ms_call * 1e-3) / 1e12
