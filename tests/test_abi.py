@@ -269,3 +269,18 @@ def test_prefix_cache_create_validation(lib):
     assert lib.mqa_prefix_cache_create(16, 0, ctypes.byref(h)) == 2
     assert lib.mqa_prefix_cache_create(16, 10, None) == 1
 
+
+
+def test_decode_plan_short_ranges(lib):
+    """The decode planner (seen through the workspace it asks for): a
+    1024-key window over 64 sequences of 32 heads runs as whole-window
+    16-head work-groups with no partition states; the same sequences' global
+    layer is split into partitions that need them; a window too wide for the
+    short-range plan, or more 16-head groups than compute units, falls back
+    to partitions. (Without a GPU the planner assumes 256 compute units.)"""
+    import mqa_attention_int8_amd as m
+    assert m.mqa_decode_workspace_bytes(64, 32, 128, 4096, 1024) == 0
+    assert m.mqa_decode_workspace_bytes(64, 32, 128, 4096, 0) > 0
+    assert m.mqa_decode_workspace_bytes(64, 32, 128, 4096, 2048) > 0      # 65 tiles: partitions
+    assert m.mqa_decode_workspace_bytes(8, 32, 128, 1000, 0) == 0         # 32 tiles, 16 groups
+    assert m.mqa_decode_workspace_bytes(200, 32, 128, 32768, 1024) > 0    # 400 groups > 256 units
