@@ -455,7 +455,9 @@ __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D /
 // depends on timing, so results can differ between runs in the last bits.
 // Each wave keeps two tiles in registers: on entry `ta` holds the loads of its
 // tile ia and `tb` those of ib (> ia); a buffer is refilled with the next
-// handed-out tile as soon as it has been consumed.
+// handed-out tile as soon as it has been consumed. That tile's index is
+// claimed before the consumed tile's arithmetic, so the counter's round trip
+// overlaps it.
 template <int D, int NT, bool Q8, typename Load>
 __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D, NT>& st, const Load& load,
                                           const QOperand<D, NT, Q8>& qop, float kscale,
@@ -464,24 +466,26 @@ __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D,
                                           int8_t* scratch, bool write, int8_t* krow, int8_t* vrow, float* ks,
                                           float* vs) {
   const int c = lane & 15;
-  const auto grab = [&]() {
+  const auto claim = [&]() {
     int r = 0;
     if (lane == 0) r = atomicAdd(next, 1);
-    return __builtin_amdgcn_readfirstlane(r);
+    return r;
   };
   // ia < ib at the top of the loop and handed-out indices only grow, so once
   // ia is past the end so is ib (and vice versa in the middle).
   while (ia < count) {
+    int na = claim();
     if (ia == new_tile)
       encode_new_row<D>(ta, xk, xv, scratch, hi - 1 - (pt0 + ia) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
     compute_tile<D, NT, Q8>(ta, st, qop, kscale, (pt0 + ia) * kTileKeys, lo, hi, g);
-    ia = grab();
+    ia = __builtin_amdgcn_readfirstlane(na);
     load(ta, ia);
     if (ib >= count) break;
+    int nb = claim();
     if (ib == new_tile)
       encode_new_row<D>(tb, xk, xv, scratch, hi - 1 - (pt0 + ib) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
     compute_tile<D, NT, Q8>(tb, st, qop, kscale, (pt0 + ib) * kTileKeys, lo, hi, g);
-    ib = grab();
+    ib = __builtin_amdgcn_readfirstlane(nb);
     load(tb, ib);
   }
 }
