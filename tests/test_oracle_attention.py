@@ -290,3 +290,26 @@ def test_int8_mqa_accounting():
     assert oracle.decode_visible_keys([4096] * 64, 0) * 264 == 69_206_016
     assert oracle.decode_visible_keys([4096] * 64, 1024) * 264 == 17_301_504
     assert oracle.prefill_visible_pairs([8192] * 16, 512, 1024) == 16 * 512 * 1024
+
+
+@pytest.mark.parametrize("window", [0, 1, 3, 7, 64, 1000])
+def test_visible_counts_brute_force(window):
+    """Key/query pair counts behind the bandwidth and flop figures, against a
+    direct count of the mask predicate (key j visible to the query at
+    absolute position p iff j <= p and, with a window W > 0, j > p - W), and
+    the closed forms: global C P + C (C + 1) / 2 per sequence; C W once the
+    prefix holds at least W keys."""
+    prefixes, C = [0, 1, 5, 9, 70], 11
+    want = 0
+    for P in prefixes:
+        for i in range(C):
+            p = P + i
+            want += sum(1 for j in range(P + C) if j <= p and (window <= 0 or j > p - window))
+    assert oracle.prefill_visible_pairs(prefixes, C, window) == want
+    if window <= 0:
+        assert want == sum(C * P + C * (C + 1) // 2 for P in prefixes)
+    for P in (window, window + 3) if window > 0 else ():
+        assert oracle.prefill_visible_pairs([P], C, window) == C * window
+    lens = [0, 1, 2, 6, 7, 8, 63, 64, 65, 999, 1000, 1001]
+    want_d = sum(sum(1 for j in range(n) if window <= 0 or j >= n - window) for n in lens)
+    assert oracle.decode_visible_keys(lens, window) == want_d
