@@ -64,7 +64,9 @@ typedef enum {
 /* Non-owning description of ONE shared KV buffer (one K/V head per token).
  * k, v: int8 [B, L_cap, D]; k_scale, v_scale: fp32 [B, L_cap] (one scale per
  * token row). Several layers may pass the same view (cross-layer sharing).
- * The struct itself lives in HOST memory and is read only during the call. */
+ * The struct itself lives in HOST memory and is read only during the call.
+ * The attention calls address one sequence's K or V rows with 32-bit byte
+ * offsets: they return SHAPE for a view with L_cap * D >= 2^32. */
 typedef struct {
   const int8_t* k;
   const int8_t* v;
@@ -177,7 +179,9 @@ size_t mqa_prefill_workspace_bytes(int32_t B, int32_t C, int32_t D,
  *                the chunk's key/value tiles converted once for the matrix
  *                cores. Calls that may run concurrently must not share it.
  * Errors: NULL, SHAPE (C<=0, max_prefix_len+C > L_cap, ...), UNSUPPORTED,
- * ALIGN, WORKSPACE, HIP. */
+ * ALIGN, WORKSPACE, HIP. SHAPE also when one sequence's converted tiles
+ * would reach 2^31 bytes: ceil((max_prefix_len + C) / 64) * (256 D + 1024)
+ * must stay below 2^31 (about 4.07 M positions at D = 128, 7.9 M at D = 64). */
 int mqa_prefill_chunk(const uint16_t* q, const mqa_kv_view* kv,
                       const int32_t* prefix_lens, int32_t max_prefix_len,
                       int32_t B, int32_t C, int32_t Hq, int32_t D,

@@ -42,7 +42,8 @@ int check_kv(const mqa_kv_view* kv, int32_t D) {
   if (kv->L_cap <= 0) return MQA_ERR_SHAPE;
   if (!aligned16(kv->k) || !aligned16(kv->v)) return MQA_ERR_ALIGN;
   if (((uintptr_t)kv->k_scale & 3u) || ((uintptr_t)kv->v_scale & 3u)) return MQA_ERR_ALIGN;
-  (void)D;
+  // the kernels address one sequence's K or V rows with 32-bit byte offsets
+  if ((int64_t)kv->L_cap * D > (int64_t)0xffffffff) return MQA_ERR_SHAPE;
   return MQA_OK;
 }
 

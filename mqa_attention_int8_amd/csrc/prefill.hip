@@ -615,6 +615,8 @@ int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& lay
   // staged tiles; one past the cache capacity past the cache.
   prm.P_max = (int)((int64_t)max_prefix_len < (int64_t)prm.L_cap - C ? max_prefix_len : prm.L_cap - C);
   const size_t tb = (D == 128) ? StagedTile<128>::kBytes : StagedTile<64>::kBytes;
+  // the attention pass addresses a sequence's staged tiles with 32-bit signed offsets
+  if ((int64_t)prm.ntiles * (int64_t)tb > (int64_t)0x7fffffff) return MQA_ERR_SHAPE;
   prm.stage = static_cast<char*>(workspace);
   prm.seq_e = reinterpret_cast<float*>(prm.stage + (size_t)B * prm.ntiles * tb);
   const int64_t rows = (int64_t)C * Hq;

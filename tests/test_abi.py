@@ -76,6 +76,9 @@ def test_decode_validation(lib):
     assert decode(lib, kv=kv(ks=FAKE + 4)) == 4
     # needs a workspace (many partitions) but none given
     assert decode(lib, kv=kv(L_cap=1 << 16), max_len=1 << 16, B=64) == 5
+    # one sequence's K rows must stay below 4 GiB (32-bit offsets)
+    assert decode(lib, kv=kv(L_cap=1 << 25), max_len=64, D=128) == 2
+    assert decode(lib, kv=kv(L_cap=1 << 26), max_len=64, D=64) == 2
 
 
 def test_quantize_validation(lib):
@@ -98,6 +101,11 @@ def test_prefill_validation(lib):
     assert f(out=FAKE + 2) == 4
     assert f(ws=None) == 5
     assert f(wsb=16) == 5
+    # a sequence's staged tiles must stay below 2^31 bytes: 63550 tiles of
+    # 33792 bytes at D = 128 is the last size that fits
+    v = kv(L_cap=1 << 24)
+    assert f(P=63551 * 64 - 20, wsb=1 << 62) == 2
+    assert f(P=123362 * 64 - 20, D=64, wsb=1 << 62) == 2   # 17408-byte tiles at D = 64
     assert f(ws=FAKE + 8) == 4
     need = lib.mqa_prefill_workspace_bytes(2, 20, 128, 10)
     assert need >= 2 * 64 * 128 * 2 * 2      # at least one converted K and V tile per sequence
