@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the hybrid/long/prefill lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
-    ap.add_argument("--only", choices=["decode", "hybrid", "long", "prefill", "paged", "q8", "prefix_cache"],
+    ap.add_argument("--only", choices=["decode", "hybrid", "long", "prefill", "paged", "q8", "prefix_cache",
+                                       "ceilings"],
                     default=None,
                     help="time a single workload (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -161,6 +162,79 @@ def bench_decode(torch, m, acct, args, stream):
         "global_GBps": kv_global / (ms_call * 1e-3) / 1e9, "rotation_copies": R,
         "graph": use_graph,
     }
+    return res
+
+
+def load_ceilings():
+    """libmqa_ceilings.so (measurement kernels); raises if it is not built."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mqa_attention_int8_amd", "libmqa_ceilings.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    lib.mqa_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+    lib.mqa_ceiling_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mqa_ceiling_mfma_bf16_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.mqa_ceiling_mfma_bf16_flops.restype = ctypes.c_double
+    return lib
+
+
+def bench_ceilings(torch, stream):
+    """Achievable ceilings on this GPU: one-pass HBM streaming (the global
+    decode call's 69.2 MB and 1 GiB, each over >= 1 GiB of rotated copies so
+    no cache holds them) and dense bf16 MFMA throughput."""
+    lib = load_ceilings()
+    sp = stream.cuda_stream
+    res = {}
+    blocks = 8192                     # fastest of 1024-16384 (non-temporal loads; plain loads were slower)
+    partial = torch.empty(blocks, dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    for name, nbytes in (("stream_read_69MB", 69_206_016), ("stream_read_1GiB", 1 << 30)):
+        R = max(2, math.ceil((1 << 30) / nbytes))
+        bufs = [torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda", generator=gen)
+                for _ in range(R)]
+        torch.cuda.synchronize()          # the fills ran on the default stream
+        with torch.cuda.stream(stream):
+            # every word read exactly once: the partial sums add up to the buffer's sum mod 2^32
+            rc = lib.mqa_ceiling_stream_read(bufs[0].data_ptr(), nbytes, blocks, partial.data_ptr(), sp)
+            if rc != 0:
+                raise RuntimeError(f"mqa_ceiling_stream_read: status {rc}")
+            torch.cuda.synchronize()
+            got = int(partial.to(torch.int64).sum().item()) & 0xFFFFFFFF
+            want = int(bufs[0].to(torch.int64).sum().item()) & 0xFFFFFFFF
+            if got != want:
+                raise RuntimeError(f"streaming checksum {got:#x} != {want:#x}")
+
+            def period():
+                for r in range(R):
+                    lib.mqa_ceiling_stream_read(bufs[r].data_ptr(), nbytes, blocks, partial.data_ptr(),
+                                                torch.cuda.current_stream().cuda_stream)
+            reps = max(2, 64 // R)
+            ms, _ = run_steps(torch, period, reps, True, stream, warm=3)
+        us = ms / (reps * R) * 1e3
+        res[name] = {"bytes": nbytes, "us": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+                     "frac_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "rotation_copies": R,
+                     "blocks": blocks}
+        del bufs
+    mb, iters = 1024, 2048
+    sink = torch.empty(mb * 512, dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(stream):
+        def mm():
+            rc = lib.mqa_ceiling_mfma_bf16(mb, iters, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"mqa_ceiling_mfma_bf16: status {rc}")
+        mm()
+        torch.cuda.synchronize()
+        if not bool(torch.isfinite(sink).all()):
+            raise RuntimeError("MFMA loop produced non-finite sums")
+        ms, _ = run_steps(torch, mm, 10, True, stream, warm=20)
+    fl = lib.mqa_ceiling_mfma_bf16_flops(mb, iters)
+    tf = fl / (ms / 10 * 1e-3) / 1e12
+    res["mfma_bf16"] = {"flops_per_launch": fl, "us": ms / 10 * 1e3, "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
+                        "kernel": "v_mfma_f32_16x16x32_bf16, 8 independent chains per wave, 8 waves per work-group, "
+                                  f"{mb} work-groups"}
     return res
 
 
@@ -553,6 +627,8 @@ def main():
             extra["q8"] = bench_q8(torch, m, acct, stream)
         if args.only in (None, "prefix_cache"):
             extra["prefix_cache"] = bench_prefix_cache(torch, m, stream)
+        if args.only in (None, "ceilings"):
+            extra["ceilings"] = bench_ceilings(torch, stream)
     if dec is None:
         print(json.dumps({"extra": extra}))
         return

@@ -16,6 +16,9 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "prefix_cache.cpp", "quantize.hip", "decode.hip", "prefill.hip", "kv_transfer.hip"]
+# Measurement kernels of the benchmark, in a library of their own.
+CEILINGS_LIB = os.path.join(PKG, "libmqa_ceilings.so")
+CEILINGS_SOURCES = ["ceilings.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -36,11 +39,18 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source and link the shared library; returns its path."""
+    """Compile and link libmqa_int8.so and libmqa_ceilings.so; returns the
+    attention library's path."""
+    _link(SOURCES, LIB, verbose, jobs)
+    _link(CEILINGS_SOURCES, CEILINGS_LIB, verbose, jobs)
+    return LIB
+
+
+def _link(sources, lib_path: str, verbose: bool, jobs: int) -> None:
     out_dir = os.path.join(PKG, "_objs")
     os.makedirs(out_dir, exist_ok=True)
     procs, objs = [], []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [hipcc(), *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -62,14 +72,13 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         for src, text in failed:
             sys.stderr.write(f"--- {src} ---\n{text}\n")
         raise RuntimeError("hipcc failed for: " + ", ".join(s for s, _ in failed))
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
            f"-L{ROCM}/lib", "-lamdhip64", "-Wl,--no-undefined"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
 
 
 if __name__ == "__main__":

@@ -17,8 +17,8 @@ def lib():
     return m.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
 
@@ -31,6 +31,32 @@ def test_every_declared_function_is_exported(lib):
             "mqa_decode_q8", "mqa_decode_append_q8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in mqa_int8.h but not exported"
+
+
+def test_ceilings_library_exports_its_header():
+    """libmqa_ceilings.so (the benchmark's measurement kernels) loads and
+    exports what include/mqa_ceilings.h declares; only invalid arguments are
+    passed, which return before any launch."""
+    path = os.path.join(ROOT, "mqa_attention_int8_amd", "libmqa_ceilings.so")
+    assert os.path.exists(path), "build first"
+    cl = ctypes.CDLL(path)
+    names = declared_functions(os.path.join(ROOT, "include", "mqa_ceilings.h"))
+    assert set(names) == {"mqa_ceiling_stream_read", "mqa_ceiling_mfma_bf16", "mqa_ceiling_mfma_bf16_flops"}
+    for n in names:
+        assert hasattr(cl, n), f"{n} declared in mqa_ceilings.h but not exported"
+    cl.mqa_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+    cl.mqa_ceiling_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    cl.mqa_ceiling_mfma_bf16_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    cl.mqa_ceiling_mfma_bf16_flops.restype = ctypes.c_double
+    fake = 1 << 20
+    assert cl.mqa_ceiling_stream_read(None, 64, 4, fake, None) == 1
+    assert cl.mqa_ceiling_stream_read(fake, 60, 4, fake, None) == 2        # not a multiple of 16
+    assert cl.mqa_ceiling_stream_read(fake + 8, 64, 4, fake, None) == 2    # misaligned
+    assert cl.mqa_ceiling_mfma_bf16(0, 4, fake, None) == 2
+    assert cl.mqa_ceiling_mfma_bf16(4, 4, None, None) == 1
+    # 8 waves x iters x 8 MFMAs of 16 x 16 x 32 multiply-adds per work-group
+    assert cl.mqa_ceiling_mfma_bf16_flops(3, 5) == 3 * 8 * 5 * 8 * 16 * 16 * 32 * 2
 
 
 def test_one_hip_runtime(lib):
