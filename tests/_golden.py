@@ -34,3 +34,25 @@ def kv_bytes():
             totals.append((int(v[0]), int(v[1]), int(v[2]), int(v[3]), int(v[4]), int(v[5]),
                            float(v[6]), int(v[7])))
     return per_token, totals
+
+
+def prefix_cache_cases():
+    """[(bs, capacity, [(op, tokens, expected)])]; op in match / insert /
+    state / evicted (see tests/golden/prefix_cache_lru.txt)."""
+    cases = []
+    for ln in _lines("prefix_cache_lru.txt"):
+        op, _, rest = ln.partition(" ")
+        if op == "case":
+            bs, cap = (int(x) for x in rest.split())
+            cases.append((bs, cap, []))
+        elif op in ("match", "insert"):
+            toks, _, res = rest.partition("=")
+            cases[-1][2].append((op, [int(x) for x in toks.split()], [int(x) for x in res.split()]))
+        elif op == "state":
+            blocks = [tuple(int(x) for x in part.split()) for part in rest.split("|")]
+            cases[-1][2].append((op, None, sorted(blocks)))
+        elif op == "evicted":
+            cases[-1][2].append((op, None, int(rest)))
+        else:
+            raise ValueError(f"prefix_cache_lru.txt: unknown line {ln!r}")
+    return cases

@@ -313,3 +313,62 @@ def test_visible_counts_brute_force(window):
     lens = [0, 1, 2, 6, 7, 8, 63, 64, 65, 999, 1000, 1001]
     want_d = sum(sum(1 for j in range(n) if window <= 0 or j >= n - window) for n in lens)
     assert oracle.decode_visible_keys(lens, window) == want_d
+
+
+# ---------------------------------------------------------------------------
+# default softmax scale: 1/sqrt(head_dim), not the model width
+# [explinks.com page, 代码块描述: the snippet divides by the square root of
+# the embedding size, which for its multi-head code is the whole model
+# width; the reading is the head dimension of the one shared head]
+# ---------------------------------------------------------------------------
+
+def test_default_softmax_scale_values():
+    assert oracle.default_softmax_scale(64) == np.float32(0.125)
+    assert oracle.default_softmax_scale(16) == np.float32(0.25)
+    # fl32(1/sqrt(128)): the fp32 nearest to 0.08838834764..., bit pattern 0x3DB504F3
+    s128 = oracle.default_softmax_scale(128)
+    assert s128.dtype == np.float32
+    assert struct.pack("<f", s128) == struct.pack("<I", 0x3DB504F3)
+
+
+@pytest.mark.parametrize("D,qlead", [(4, 2.0), (64, 8.0), (16, 4.0)])
+def test_default_scale_inside_attention_closed_form(D, qlead):
+    """Two keys: k_0 = 0, k_1 = e_0 (code 1, scale 1); values v_0 = 0, v_1 =
+    all ones. With q = qlead * e_0 and qlead = sqrt(D), the logits are 0 and
+    qlead / sqrt(D) = 1, so every output column is e / (1 + e). A scale of
+    1/D, or 1/sqrt(Hq * D), or none at all gives another value."""
+    Hq = 3
+    q = np.zeros((1, Hq, D), np.uint16)
+    q[0, :, 0] = synth.f32_to_bf16_bits(np.float32(qlead))
+    kq = np.zeros((1, 2, D), np.int8)
+    kq[0, 1, 0] = 1
+    ks = np.array([[0.0, 1.0]], np.float32)
+    vq = np.zeros((1, 2, D), np.int8)
+    vq[0, 1, :] = 1
+    vs = np.array([[0.0, 1.0]], np.float32)
+    out = oracle.decode_ref(q, kq, ks, vq, vs, np.array([2], np.int32), 0)
+    want = math.e / (1.0 + math.e)
+    # sigma = fl32(1/sqrt(D)) is exact for these D
+    assert np.max(np.abs(out - want)) <= 1e-15
+    rows = oracle.decode_ref_rows(q, kq, ks, vq, vs, np.array([2], np.int32), 0, [(0, 1)])
+    assert np.max(np.abs(rows - want)) <= 1e-15
+
+
+# ---------------------------------------------------------------------------
+# decode_ref_rows (the sampled-row checker) against scalar brute force
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("window", [0, 1, 5])
+def test_decode_rows_brute_force(window):
+    B, L, Hq, D = 5, 30, 3, 8
+    q, kq, ks, vq, vs, lens = make_case(21, B, L, Hq, D, lens=[0, 1, 4, 17, 30])
+    sigma = float(oracle.default_softmax_scale(D))
+    bf = brute_decode(q, kq, ks, vq, vs, lens, window, sigma)
+    picks = [(b, h) for b in range(B) for h in range(Hq)][::-1] + [(3, 1), (0, 0)]
+    got = oracle.decode_ref_rows(q, kq, ks, vq, vs, lens, window, picks)
+    assert got.shape == (len(picks), D)
+    for i, (b, h) in enumerate(picks):
+        assert np.max(np.abs(got[i] - bf[b, h])) <= 1e-12, (b, h)
+    # the empty sequence (n = 0) gives a zero row
+    assert not got[picks.index((0, 0))].any()
+    assert oracle.decode_ref_rows(q, kq, ks, vq, vs, lens, window, []).shape == (0, D)

@@ -78,3 +78,46 @@ def test_hit_rate_of_a_long_conversation():
         cache.insert(hist)
     st = cache.stats()
     assert st["matched_tokens"] / st["lookup_tokens"] > 0.8
+
+
+def _golden_cases():
+    from _golden import prefix_cache_cases
+    return prefix_cache_cases()
+
+
+@pytest.mark.parametrize("ci", [0, 1])
+def test_model_follows_hand_worked_sequence(ci):
+    """The policy model against a sequence worked out by hand: a partial
+    match, evictions of the least recently used leaf (not the oldest block),
+    a cascade where a parent becomes the next leaf, and an insert that stops
+    instead of evicting its own chain."""
+    bs, cap, ops = _golden_cases()[ci]
+    ref = PrefixCacheRef(bs, cap)
+    for i, (op, toks, want) in enumerate(ops):
+        if op == "match":
+            assert ref.match(toks) == want[0], (i, op, toks)
+        elif op == "insert":
+            assert list(ref.insert(toks)) == want, (i, op, toks)
+        elif op == "state":
+            assert sorted(ref.last_use) == want, i
+        else:
+            assert ref.evicted == want, i
+
+
+@pytest.mark.parametrize("ci", [0, 1])
+def test_library_follows_hand_worked_sequence(ci):
+    import mqa_attention_int8_amd as m
+    bs, cap, ops = _golden_cases()[ci]
+    cache = m.PrefixCache(bs, cap)
+    for i, (op, toks, want) in enumerate(ops):
+        if op == "match":
+            got, _ = cache.match(toks)
+            assert got == want[0], (i, op, toks)
+        elif op == "insert":
+            _, first, n = cache.insert(toks)
+            assert [first, n] == want, (i, op, toks)
+        elif op == "state":
+            assert cache.stats()["used_blocks"] == len(want), i
+        else:
+            assert cache.stats()["evicted_blocks"] == want, i
+    cache.close()
