@@ -1,23 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of MQA int8-KV decode on one MI355X.
 
-One step = one decode step of two attention layers that share ONE int8 KV
-buffer (cross-layer KV sharing): the global layer owns the buffer and runs
-mqa_decode_append (the new token's K and V rows are encoded into it in the
-same launch), then the sliding-window (1024) layer runs mqa_decode over it.
-Shapes: B = 64 sequences of 4096 keys, 32 query heads, one KV head,
-head_dim 128.
+One step = one decode step of the hybrid 6-layer block: layer 0 is global
+over buffer G, layers 1-3 use a 1024-key sliding window over buffer A,
+layers 4-5 over buffer B (cross-layer KV sharing: the first layer of each
+group appends the new token's K and V to its buffer in the same launch,
+mqa_decode_append; the others read it, mqa_decode). B = 128 sequences with
+ragged lengths uniform on [1024, 32768] (seeded), 32 query heads, one KV
+head, head_dim 128.
 
 Inputs are synthetic (seeded N(0,1) on the device, K/V encoded with the
-library's own quantizer) and resident in HBM before timing. The step is
-rotated over enough buffer copies (>= 1 GB) that the 256 MB Infinity Cache
-cannot serve the KV reads. Steps are captured in a HIP graph so the timing is
-the GPU's, not Python's.
+library's own quantizer) and resident in HBM before timing. The three
+buffers hold 3.2 GB, and one block step reads 744 MB of them, well beyond the
+256 MB Infinity Cache; layers 2, 3 and 5 re-read the window a previous layer
+of the step just read, which the cache may serve (the real schedule). Steps
+are captured in a HIP graph so the timing is the GPU's, not Python's.
 
-Prints ONE JSON line. ``value`` = decode tokens/s of the step (B tokens per
-step, attention only). ``roofline`` describes the global-layer call
-(partition kernel with the fused append + merge kernel). ``cpu_baseline`` times the CPU oracle
-on a bounded sample of the same workload.
+Prints ONE JSON line. ``value`` = decode tokens/s of the block step (B tokens
+per step, attention only: no projections or MLP). ``roofline`` describes the
+block's dominant call, the global layer (decode partition kernel with the
+fused append + merge kernel). ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload. ``extra`` holds the per-layer times
+(flushed and in the block's order), the two-layer decode step (64 x 4096
+keys), the long context (8 x 131072 keys), prefill, paged and int8-query
+variants, the host prefix cache and the measured ceilings.
 """
 from __future__ import annotations
 
@@ -25,47 +31,68 @@ import argparse
 import json
 import math
 import os
+import platform
+import statistics
 import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, datasheet
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, datasheet
 METRIC = "MQA int8-KV decode: KV-read HBM GB/s (% of peak) and decode tokens/s"
+MIN_REPLAYS = 20                # individually timed replays behind every median
+DTYPE = ("int8 KV with fp32 per-token scales; bf16 q; exact int8 operands on fp16 MFMA, "
+         "P'' as fp16 hi+lo; fp32 softmax and accumulation; fp32 out")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
-    ap.add_argument("--no-extra", action="store_true", help="skip the hybrid/long/prefill lines")
+    ap.add_argument("--steps", type=int, default=50, help="block steps timed for the headline value")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed block steps before timing")
+    ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
-    ap.add_argument("--only", choices=["decode", "hybrid", "long", "prefill", "paged", "q8", "prefix_cache",
-                                       "ceilings"],
-                    default=None,
-                    help="time a single workload (for profiling runs)")
+    ap.add_argument("--only", choices=["hybrid", "hybrid_global", "decode", "long", "prefill", "paged", "q8",
+                                       "prefix_cache", "ceilings"],
+                    default=None, help="time a single workload (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
 
 
-class Timer:
-    """HIP events on the stream the kernels run on."""
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
 
-    def __init__(self, torch, stream):
-        self.torch, self.stream = torch, stream
-        self.a = torch.cuda.Event(enable_timing=True)
-        self.b = torch.cuda.Event(enable_timing=True)
+def capture(torch, fn, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    return g
 
-    def start(self):
-        self.a.record(self.stream)
 
-    def stop_ms(self):
-        self.b.record(self.stream)
-        self.b.synchronize()
-        return self.a.elapsed_time(self.b)
+def replay_times(torch, g, stream, reps, warm):
+    """`warm` untimed replays, then `reps` replays each bracketed by its own
+    HIP event pair on `stream` (the stream the graph's kernels run on).
+    Returns the list of milliseconds per replay."""
+    for _ in range(warm):
+        g.replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def summary(ms_list, per=1):
+    """Median, mean, min and max of per-replay times, divided by `per` calls per replay, in us."""
+    us = sorted(m * 1e3 / per for m in ms_list)
+    return {"median_us": statistics.median(us), "mean_us": statistics.fmean(us), "min_us": us[0],
+            "max_us": us[-1], "replays": len(us)}
 
 
 def make_decode_buffers(torch, m, B, L, D, copies, gen):
@@ -85,85 +112,224 @@ def make_decode_buffers(torch, m, B, L, D, copies, gen):
     return bufs
 
 
-def run_steps(torch, fn, steps, use_graph, stream, warm=1):
-    """Replay `fn` (which runs `period` steps) steps/period times after `warm`
-    untimed replays; returns ms."""
-    timer = Timer(torch, stream)
-    if use_graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            fn()
-        torch.cuda.synchronize()
-        reps = steps
-        for _ in range(max(1, warm)):
-            g.replay()
-        torch.cuda.synchronize()
-        timer.start()
-        for _ in range(reps):
-            g.replay()
-        ms = timer.stop_ms()
-        return ms, g
-    timer.start()
-    for _ in range(steps):
-        fn()
-    return timer.stop_ms(), None
+def rotation(bytes_per_copy):
+    """Copies of a call's inputs that add up to >= 1 GiB (beyond the Infinity Cache)."""
+    return max(2, math.ceil((1 << 30) / bytes_per_copy))
 
 
-def bench_decode(torch, m, acct, args, stream):
+# ---------------------------------------------------------------------------
+# headline: the hybrid 6-layer block (ragged 1024..32768 keys, 3 shared buffers)
+# ---------------------------------------------------------------------------
+
+def bench_hybrid(torch, m, acct, args, stream):
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import synth
+    w = synth.HYBRID
+    B, Hq, D = w.B, w.Hq, w.D
+    lens = w.lens()
+    L = int(lens.max())
+    L_cap = (L + 31) // 32 * 32
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    bufs = {name: make_decode_buffers(torch, m, B, L_cap, D, 1, gen)[0] for name in ("G", "A", "Bf")}
+    seq_lens = torch.from_numpy(lens).cuda()
+    q = [torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in w.layers]
+    knew = torch.randn((B, D), generator=gen, device="cuda")
+    vnew = torch.randn((B, D), generator=gen, device="cuda")
+    out = torch.empty((B, Hq, D), device="cuda")
+    ws = torch.zeros(max(m.mqa_decode_workspace_bytes(B, Hq, D, L, win) for _, win in w.layers) + 16,
+                     dtype=torch.uint8, device="cuda")
+    owners = {}
+    for li, (name, _) in enumerate(w.layers):
+        owners.setdefault(name, li)
+
+    def layer(li):
+        name, win = w.layers[li]
+        kv = bufs[name]
+        if owners[name] == li:             # first layer of a sharing group writes the token (fused)
+            m.mqa_decode_append(q[li], kv, knew, vnew, seq_lens, L, win, out=out, workspace=ws)
+        else:
+            m.mqa_decode(q[li], kv, seq_lens, L, win, out=out, workspace=ws)
+
+    def block():
+        for li in range(len(w.layers)):
+            layer(li)
+
+    kv_layers = [acct.decode_kv_bytes(lens, win, D) for _, win in w.layers]
+    kv_block = sum(kv_layers)
+    res = {"workload": w.name, "B": B, "Hq": Hq, "D": D, "seq_len_range": [int(lens.min()), int(lens.max())],
+           "layers": [{"buffer": n, "window": win} for n, win in w.layers], "kv_bytes_per_step": kv_block}
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            block()
+        torch.cuda.synchronize()
+        g = capture(torch, block, stream)
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        # headline: exactly `steps` block steps between two events, synchronised on both sides
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms_total = a.elapsed_time(b)
+        res["steps_timed"] = args.steps
+        res["ms_per_step"] = ms_total / args.steps
+        res["block_step"] = summary(replay_times(torch, g, stream, max(MIN_REPLAYS, 20), 2))
+        del g
+        # the global layer's call alone (the dominant call): replays of one call
+        gg = capture(torch, lambda: layer(0), stream)
+        res["global_call"] = summary(replay_times(torch, gg, stream, max(MIN_REPLAYS, 30), 3))
+        del gg
+        # per layer: after a 1 GiB write (HBM figure) and right after the previous
+        # layer of the block (the real schedule; layers 2, 3, 5 re-read a window)
+        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        per_layer = []
+        for li in range(len(w.layers)):
+            fl, un = [], []
+            for r in range(MIN_REPLAYS):
+                for kind in ("flushed", "after_previous_layer"):
+                    flush_buf.fill_(float(r))
+                    if kind == "after_previous_layer":
+                        layer((li - 1) % len(w.layers))
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    layer(li)
+                    e1.record(stream)
+                    (fl if kind == "flushed" else un).append((e0, e1))
+            torch.cuda.synchronize()
+            f = summary([x.elapsed_time(y) for x, y in fl])
+            u = summary([x.elapsed_time(y) for x, y in un])
+            name, win = w.layers[li]
+            per_layer.append({"layer": li, "buffer": name, "window": win, "kv_bytes": kv_layers[li],
+                              "flushed_us": f["median_us"], "after_previous_layer_us": u["median_us"],
+                              "flushed_GBps": kv_layers[li] / (f["median_us"] * 1e-6) / 1e9,
+                              "after_previous_layer_GBps": kv_layers[li] / (u["median_us"] * 1e-6) / 1e9})
+        del flush_buf
+    res["per_layer"] = per_layer
+    res["tokens_per_s"] = B / (res["ms_per_step"] * 1e-3)
+    res["kv_GBps"] = kv_block / (res["ms_per_step"] * 1e-3) / 1e9
+    res["global_kv_bytes"] = kv_layers[0]
+    res["global_GBps"] = kv_layers[0] / (res["global_call"]["mean_us"] * 1e-6) / 1e9
+    res["note"] = ("per-layer times are eager calls bracketed by events, each after a 1 GiB write (flushed) "
+                   "or after the block's previous layer; the block step is one graph replay")
+    return res
+
+
+def bench_hybrid_global_only(torch, m, stream, calls=8):
+    """The hybrid block's global-layer call alone, a few times (for counter runs)."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import synth
+    w = synth.HYBRID
+    B, Hq, D = w.B, w.Hq, w.D
+    lens = w.lens()
+    L = int(lens.max())
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    kv = make_decode_buffers(torch, m, B, (L + 31) // 32 * 32, D, 1, gen)[0]
+    seq_lens = torch.from_numpy(lens).cuda()
+    q = torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    knew = torch.randn((B, D), generator=gen, device="cuda")
+    vnew = torch.randn((B, D), generator=gen, device="cuda")
+    out = torch.empty((B, Hq, D), device="cuda")
+    ws = m.decode_workspace(B, Hq, D, L, 0)
+    with torch.cuda.stream(stream):
+        for _ in range(calls):
+            m.mqa_decode_append(q, kv, knew, vnew, seq_lens, L, 0, out=out, workspace=ws)
+        torch.cuda.synchronize()
+    return {"workload": w.name + " global layer", "calls": calls}
+
+
+# ---------------------------------------------------------------------------
+# the two-layer decode step: 64 sequences x 4096 keys, global + window 1024
+# ---------------------------------------------------------------------------
+
+def bench_decode(torch, m, acct, stream):
     B, Hq, D, L = 64, 32, 128, 4096
     windows = (0, 1024)
-    bytes_per_copy = B * L * (2 * D + 8)
-    R = max(2, math.ceil((1 << 30) / bytes_per_copy))              # >= 1 GiB of KV
+    R = rotation(B * L * (2 * D + 8))
     gen = torch.Generator(device="cuda")
     gen.manual_seed(2)
     bufs = make_decode_buffers(torch, m, B, L, D, R, gen)
     seq_lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
     q = [[torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in windows]
          for _ in range(R)]
-    knew = [torch.randn((B, 1, D), generator=gen, device="cuda") for _ in range(R)]
-    vnew = [torch.randn((B, 1, D), generator=gen, device="cuda") for _ in range(R)]
+    knew = [torch.randn((B, D), generator=gen, device="cuda") for _ in range(R)]
+    vnew = [torch.randn((B, D), generator=gen, device="cuda") for _ in range(R)]
     outs = [torch.empty((B, Hq, D), device="cuda") for _ in windows]
     ws = [m.decode_workspace(B, Hq, D, L, w) for w in windows]
 
-    def one_step(r):
+    def step(r):
         # the global layer owns the buffer: it appends the new token (fused), the window layer reads it
-        kv = bufs[r]
-        m.mqa_decode_append(q[r][0], kv, knew[r].view(B, D), vnew[r].view(B, D), seq_lens, L, windows[0],
-                            out=outs[0], workspace=ws[0])
-        m.mqa_decode(q[r][1], kv, seq_lens, L, windows[1], out=outs[1], workspace=ws[1])
+        m.mqa_decode_append(q[r][0], bufs[r], knew[r], vnew[r], seq_lens, L, windows[0], out=outs[0],
+                            workspace=ws[0])
+        m.mqa_decode(q[r][1], bufs[r], seq_lens, L, windows[1], out=outs[1], workspace=ws[1])
 
     def period():
         for r in range(R):
-            one_step(r)
+            step(r)
 
     def global_only():
         for r in range(R):
-            m.mqa_decode_append(q[r][0], bufs[r], knew[r].view(B, D), vnew[r].view(B, D), seq_lens, L, 0,
-                                out=outs[0], workspace=ws[0])
+            m.mqa_decode_append(q[r][0], bufs[r], knew[r], vnew[r], seq_lens, L, 0, out=outs[0], workspace=ws[0])
 
+    def window_only():
+        for r in range(R):
+            m.mqa_decode(q[r][1], bufs[r], seq_lens, L, windows[1], out=outs[1], workspace=ws[1])
+
+    res = {"workload": "decode_B64_Hq32_D128_L4096: append + global layer + window-1024 layer sharing one "
+                       "int8 KV buffer", "rotation_copies": R}
     with torch.cuda.stream(stream):
-        for _ in range(max(1, args.warmup // R)):
-            period()
+        period()
         torch.cuda.synchronize()
-        use_graph = not args.no_graph
-        reps = max(1, args.steps // R)
-        ms, _ = run_steps(torch, period, reps, use_graph, stream)
-        steps_done = reps * R
-        ms_step = ms / steps_done
-        # dominant kernel: the global layer's call (fused append + partitions, then the merge)
-        ms_g, _ = run_steps(torch, global_only, reps, use_graph, stream)
-        ms_call = ms_g / (reps * R)
-    kv_step = sum(acct.decode_kv_bytes([L] * B, w, D) for w in windows)
-    kv_global = acct.decode_kv_bytes([L] * B, 0, D)
-    res = {
-        "steps_done": steps_done, "ms_per_step": ms_step, "tokens_per_s": B / (ms_step * 1e-3),
-        "kv_bytes_per_step": kv_step, "step_kv_GBps": kv_step / (ms_step * 1e-3) / 1e9,
-        "global_call_us": ms_call * 1e3, "global_kv_bytes": kv_global,
-        "global_GBps": kv_global / (ms_call * 1e-3) / 1e9, "rotation_copies": R,
-        "graph": use_graph,
-    }
+        for name, fn in (("step", period), ("global_call", global_only), ("window_call", window_only)):
+            g = capture(torch, fn, stream)
+            res[name] = summary(replay_times(torch, g, stream, MIN_REPLAYS, 3), per=R)
+            del g
+    kv_g = acct.decode_kv_bytes([L] * B, 0, D)
+    kv_w = acct.decode_kv_bytes([L] * B, 1024, D)
+    res["tokens_per_s"] = B / (res["step"]["median_us"] * 1e-6)
+    res["global_kv_bytes"], res["window_kv_bytes"] = kv_g, kv_w
+    res["global_GBps"] = kv_g / (res["global_call"]["median_us"] * 1e-6) / 1e9
+    res["window_GBps"] = kv_w / (res["window_call"]["median_us"] * 1e-6) / 1e9
+    res["global_frac_hbm_peak"] = res["global_GBps"] / HBM_PEAK_GBPS
+    res["window_frac_hbm_peak"] = res["window_GBps"] / HBM_PEAK_GBPS
+    res["global_traffic_bytes"] = counted_traffic("decode_global_traffic.json")
     return res
 
+
+def bench_long(torch, m, acct, stream):
+    B, Hq, D, L = 8, 32, 128, 131072
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    R = rotation(B * L * (2 * D + 8))
+    bufs = make_decode_buffers(torch, m, B, L, D, R, gen)
+    seq_lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    q = torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((B, Hq, D), device="cuda")
+    ws = m.decode_workspace(B, Hq, D, L, 0)
+
+    def calls():
+        for kv in bufs:
+            m.mqa_decode(q, kv, seq_lens, L, 0, out=out, workspace=ws)
+
+    with torch.cuda.stream(stream):
+        calls()
+        torch.cuda.synchronize()
+        g = capture(torch, calls, stream)
+        s = summary(replay_times(torch, g, stream, MIN_REPLAYS, 2), per=len(bufs))
+        del g
+    kv = acct.decode_kv_bytes([L] * B, 0, D)
+    return {"workload": "long_decode_B8_Hq32_D128_L131072", "call": s, "rotation_copies": R,
+            "tokens_per_s": B / (s["median_us"] * 1e-6), "kv_GBps": kv / (s["median_us"] * 1e-6) / 1e9,
+            "frac_hbm_peak": kv / (s["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+
+
+# ---------------------------------------------------------------------------
+# ceilings: one-pass streaming and dense MFMA on this GPU
+# ---------------------------------------------------------------------------
 
 def load_ceilings():
     """libmqa_ceilings.so (measurement kernels); raises if it is not built."""
@@ -181,24 +347,26 @@ def load_ceilings():
 
 
 def bench_ceilings(torch, stream):
-    """Achievable ceilings on this GPU: one-pass HBM streaming (the global
-    decode call's 69.2 MB and 1 GiB, each over >= 1 GiB of rotated copies so
-    no cache holds them) and dense bf16 MFMA throughput."""
+    """Achievable ceilings on this GPU: one-pass HBM streaming of the decode
+    calls' byte counts (window layer 17.3 MB, hybrid window layer 34.6 MB,
+    global layer 69.2 MB) and of 1 GiB, each over >= 1 GiB of rotated copies
+    so no cache holds them, and dense bf16 MFMA throughput."""
     lib = load_ceilings()
-    sp = stream.cuda_stream
     res = {}
     blocks = 4096                     # 16 KB chunks per work-group; the fastest of 2048-16384 on 69 MB
     partial = torch.empty(blocks, dtype=torch.int32, device="cuda")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
-    for name, nbytes in (("stream_read_69MB", 69_206_016), ("stream_read_1GiB", 1 << 30)):
-        R = max(2, math.ceil((1 << 30) / nbytes))
+    for name, nbytes in (("stream_read_17MB", 17_301_504), ("stream_read_35MB", 34_603_008),
+                         ("stream_read_69MB", 69_206_016), ("stream_read_1GiB", 1 << 30)):
+        R = rotation(nbytes)
         bufs = [torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda", generator=gen)
                 for _ in range(R)]
         torch.cuda.synchronize()          # the fills ran on the default stream
         with torch.cuda.stream(stream):
             # every word read exactly once: the partial sums add up to the buffer's sum mod 2^32
-            rc = lib.mqa_ceiling_stream_read(bufs[0].data_ptr(), nbytes, blocks, partial.data_ptr(), sp)
+            rc = lib.mqa_ceiling_stream_read(bufs[0].data_ptr(), nbytes, blocks, partial.data_ptr(),
+                                             stream.cuda_stream)
             if rc != 0:
                 raise RuntimeError(f"mqa_ceiling_stream_read: status {rc}")
             torch.cuda.synchronize()
@@ -211,12 +379,12 @@ def bench_ceilings(torch, stream):
                 for r in range(R):
                     lib.mqa_ceiling_stream_read(bufs[r].data_ptr(), nbytes, blocks, partial.data_ptr(),
                                                 torch.cuda.current_stream().cuda_stream)
-            reps = max(2, 64 // R)
-            ms, _ = run_steps(torch, period, reps, True, stream, warm=3)
-        us = ms / (reps * R) * 1e3
-        res[name] = {"bytes": nbytes, "us": us, "GBps": nbytes / (us * 1e-6) / 1e9,
-                     "frac_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "rotation_copies": R,
-                     "blocks": blocks}
+            g = capture(torch, period, stream)
+            s = summary(replay_times(torch, g, stream, MIN_REPLAYS, 3), per=R)
+            del g
+        res[name] = {"bytes": nbytes, "us": s["median_us"], "GBps": nbytes / (s["median_us"] * 1e-6) / 1e9,
+                     "frac_hbm_peak": nbytes / (s["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                     "rotation_copies": R, "blocks": blocks}
         del bufs
     mb, iters = 1024, 2048
     sink = torch.empty(mb * 512, dtype=torch.float32, device="cuda")
@@ -229,88 +397,24 @@ def bench_ceilings(torch, stream):
         torch.cuda.synchronize()
         if not bool(torch.isfinite(sink).all()):
             raise RuntimeError("MFMA loop produced non-finite sums")
-        ms, _ = run_steps(torch, mm, 10, True, stream, warm=20)
+        g = capture(torch, mm, stream)
+        s = summary(replay_times(torch, g, stream, MIN_REPLAYS, 20))
+        del g
     fl = lib.mqa_ceiling_mfma_bf16_flops(mb, iters)
-    tf = fl / (ms / 10 * 1e-3) / 1e12
-    res["mfma_bf16"] = {"flops_per_launch": fl, "us": ms / 10 * 1e3, "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
-                        "kernel": "v_mfma_f32_16x16x32_bf16, 8 independent chains per wave, 8 waves per work-group, "
-                                  f"{mb} work-groups"}
+    tf = fl / (s["median_us"] * 1e-6) / 1e12
+    res["mfma_bf16"] = {"flops_per_launch": fl, "us": s["median_us"], "TFLOPs": tf,
+                        "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
+                        "kernel": "v_mfma_f32_16x16x32_bf16, 8 independent chains per wave, 8 waves per "
+                                  f"work-group, {mb} work-groups"}
     return res
 
 
-def bench_hybrid(torch, m, acct, stream):
-    """6-layer block: 1 global + 5 window-1024 layers, buffers G (l0), A (l1-3), B (l4-5)."""
-    import numpy as np
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-    import synth
-    w = synth.HYBRID
-    B, Hq, D = w.B, w.Hq, w.D
-    lens = w.lens()
-    L = int(lens.max())
-    L_cap = (L + 15) // 16 * 16
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(3)
-    bufs = {name: make_decode_buffers(torch, m, B, L_cap, D, 1, gen)[0] for name in ("G", "A", "Bf")}
-    seq_lens = torch.from_numpy(lens).cuda()
-    q = [torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in w.layers]
-    knew = torch.randn((B, D), generator=gen, device="cuda")
-    vnew = torch.randn((B, D), generator=gen, device="cuda")
-    out = torch.empty((B, Hq, D), device="cuda")
-    ws = torch.zeros(max(m.mqa_decode_workspace_bytes(B, Hq, D, L, win) for _, win in w.layers) + 16,
-                     dtype=torch.uint8, device="cuda")
-    owners = {}
-    for li, (name, _) in enumerate(w.layers):
-        owners.setdefault(name, li)
-
-    def block():
-        for li, (name, win) in enumerate(w.layers):
-            kv = bufs[name]
-            if owners[name] == li:             # first layer of a sharing group writes the token (fused)
-                m.mqa_decode_append(q[li], kv, knew, vnew, seq_lens, L, win, out=out, workspace=ws)
-            else:
-                m.mqa_decode(q[li], kv, seq_lens, L, win, out=out, workspace=ws)
-
-    with torch.cuda.stream(stream):
-        for _ in range(3):
-            block()
-        torch.cuda.synchronize()
-        reps = 30
-        ms, _ = run_steps(torch, block, reps, True, stream)
-    ms_block = ms / reps
-    kv = sum(acct.decode_kv_bytes(lens, win, D) for _, win in w.layers)
-    return {"workload": w.name, "ms_per_block_step": ms_block, "tokens_per_s": B / (ms_block * 1e-3),
-            "kv_bytes": kv, "kv_GBps": kv / (ms_block * 1e-3) / 1e9,
-            "note": "layers 2,3,5 re-read a buffer the previous layer just read (Infinity Cache may serve them)"}
-
-
-def bench_long(torch, m, acct, stream):
-    B, Hq, D, L = 8, 32, 128, 131072
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(5)
-    bufs = make_decode_buffers(torch, m, B, L, D, 4, gen)
-    seq_lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
-    q = torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
-    out = torch.empty((B, Hq, D), device="cuda")
-    ws = m.decode_workspace(B, Hq, D, L, 0)
-
-    def calls():
-        for kv in bufs:
-            m.mqa_decode(q, kv, seq_lens, L, 0, out=out, workspace=ws)
-
-    with torch.cuda.stream(stream):
-        calls()
-        torch.cuda.synchronize()
-        reps = 25
-        ms, _ = run_steps(torch, calls, reps, True, stream)
-    ms_call = ms / (reps * len(bufs))
-    kv = acct.decode_kv_bytes([L] * B, 0, D)
-    return {"workload": "long_decode_B8_Hq32_D128_L131072", "us_per_call": ms_call * 1e3,
-            "tokens_per_s": B / (ms_call * 1e-3), "kv_GBps": kv / (ms_call * 1e-3) / 1e9,
-            "frac_hbm_peak": kv / (ms_call * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-
+# ---------------------------------------------------------------------------
+# other paths of the library
+# ---------------------------------------------------------------------------
 
 def bench_paged(torch, m, acct, stream):
-    """Paged layouts on the decode workload's shape: the global layer (fused
+    """Paged layouts on the decode step's shape: the global layer (fused
     append) over a pool of 32-token blocks in shuffled order, and a window-1024
     layer over a ring of 1024 slots per sequence; each against the same call on
     contiguous buffers, timed in this run."""
@@ -318,8 +422,7 @@ def bench_paged(torch, m, acct, stream):
     TL = L // bs
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
-    per = B * L * (2 * D + 8)
-    R = max(2, math.ceil((1 << 30) / per))
+    R = rotation(B * L * (2 * D + 8))
     cont = make_decode_buffers(torch, m, B, L, D, R, gen)
     pools = []
     for kv in cont:
@@ -336,8 +439,7 @@ def bench_paged(torch, m, acct, stream):
         pools.append(m.PagedKV(pk, pv, pks, pvs, table))
     # window-only ring buffers: 1024 slots per sequence, positions 0..L-1 appended in order
     TLr = W // bs
-    ring_per = B * W * (2 * D + 8)
-    Rr = max(2, math.ceil((1 << 30) / ring_per))
+    Rr = rotation(B * W * (2 * D + 8))
     rings = []
     for _ in range(Rr):
         table = torch.randperm(B * TLr, generator=gen, device="cuda").view(B, TLr).to(torch.int32).contiguous()
@@ -378,9 +480,9 @@ def bench_paged(torch, m, acct, stream):
                             ("window_contiguous_us", w_cont, R), ("window_ring_us", w_ring, Rr)):
             fn()
             torch.cuda.synchronize()
-            reps = 20
-            ms, _ = run_steps(torch, fn, reps, True, stream)
-            res[name] = ms * 1e3 / (reps * n)
+            g = capture(torch, fn, stream)
+            res[name] = summary(replay_times(torch, g, stream, MIN_REPLAYS, 2), per=n)["median_us"]
+            del g
     kv_g = acct.decode_kv_bytes([L] * B, 0, D)
     kv_w = acct.decode_kv_bytes([L] * B, W, D)
     res["global_paged_GBps"] = kv_g / (res["global_paged_us"] * 1e-6) / 1e9
@@ -390,15 +492,15 @@ def bench_paged(torch, m, acct, stream):
 
 
 def bench_q8(torch, m, acct, stream):
-    """The decode step of the main workload with int8 queries (int8 MFMA for
-    Q K^T; the query rows encoded by kv_quantize_int8 outside the timed
-    region, as a projection with int8 outputs would deliver them), against the
-    bf16-query step in the same run."""
+    """The two-layer decode step with int8 queries (int8 MFMA for Q K^T; the
+    query rows encoded by kv_quantize_int8 outside the timed region, as a
+    projection with int8 outputs would deliver them), against the bf16-query
+    step in the same run."""
     B, Hq, D, L = 64, 32, 128, 4096
     windows = (0, 1024)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(8)
-    R = max(2, math.ceil((1 << 30) / (B * L * (2 * D + 8))))
+    R = rotation(B * L * (2 * D + 8))
     bufs = make_decode_buffers(torch, m, B, L, D, R, gen)
     seq_lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
     zero = torch.zeros(B, dtype=torch.int32, device="cuda")
@@ -431,9 +533,9 @@ def bench_q8(torch, m, acct, stream):
         for name, fn in (("step_bf16_us", step_bf16), ("step_q8_us", step_q8), ("global_q8_us", global_q8)):
             fn()
             torch.cuda.synchronize()
-            reps = 20
-            ms, _ = run_steps(torch, fn, reps, True, stream)
-            res[name] = ms * 1e3 / (reps * R)
+            g = capture(torch, fn, stream)
+            res[name] = summary(replay_times(torch, g, stream, MIN_REPLAYS, 2), per=R)["median_us"]
+            del g
     res["tokens_per_s_q8"] = B / (res["step_q8_us"] * 1e-6)
     kv_g = acct.decode_kv_bytes([L] * B, 0, D)
     res["global_q8_GBps"] = kv_g / (res["global_q8_us"] * 1e-6) / 1e9
@@ -446,7 +548,6 @@ def bench_prefix_cache(torch, m, stream):
     control plane on a synthetic multi-turn stream (conversations of ~180
     messages, the pages' average; the hit rate is a property of this stream,
     not a claim about real traffic)."""
-    import time
     import numpy as np
     B, D, bs, L, nb = 4, 128, 32, 8192, 3
     bufs = [m.KVView.empty(B, L, D) for _ in range(nb)]
@@ -460,19 +561,21 @@ def bench_prefix_cache(torch, m, stream):
     slots = np.arange(n_blocks, dtype=np.int64)
     nbytes = n_blocks * m.kv_block_bytes(nb, bs, D)
     res = {"prefix_tokens": L, "buffers": nb, "block_size": bs, "bytes": nbytes}
-    timer = Timer(torch, stream)
     with torch.cuda.stream(stream):
         for name, fn in (("store", m.mqa_kv_blocks_to_host), ("restore", m.mqa_kv_blocks_to_device)):
             for _ in range(3):
                 fn(bufs, 1, 0, slots, bs, pool, stream=stream)
             torch.cuda.synchronize()
-            reps = 20
-            timer.start()
-            for _ in range(reps):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(MIN_REPLAYS)]
+            for a, b in ev:
+                a.record(stream)
                 fn(bufs, 1, 0, slots, bs, pool, stream=stream)
-            ms = timer.stop_ms() / reps
-            res[name + "_us"] = ms * 1e3
-            res[name + "_GBps"] = nbytes / (ms * 1e-3) / 1e9
+                b.record(stream)
+            torch.cuda.synchronize()
+            us = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+            res[name + "_us"] = us
+            res[name + "_GBps"] = nbytes / (us * 1e-6) / 1e9
     # control plane on a synthetic stream
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import synth
@@ -512,25 +615,29 @@ def bench_prefill(torch, m, acct, stream):
                 m.mqa_prefill_chunk(q, kv, plens, P, win, out=out, workspace=ws)
             call()
             torch.cuda.synchronize()
-            # untimed replays first (~0.1 s): the first ~50 ms of back-to-back
-            # calls of this MFMA-bound kernel run up to ~15% slower than the
-            # settled rate
-            reps = 10
-            ms, _ = run_steps(torch, call, reps, True, stream, warm=80 if win == 0 else 200)
-            ms_call = ms / reps
+            g = capture(torch, call, stream)
+            # the first untimed replay is timed too (cold: right after an idle GPU)
+            cold = replay_times(torch, g, stream, 1, 0)[0]
+            # then ~0.1 s of untimed replays: the first ~50 ms of back-to-back calls
+            # of this MFMA-bound kernel run up to ~15% slower than the settled rate
+            s = summary(replay_times(torch, g, stream, MIN_REPLAYS, 80 if win == 0 else 200))
+            del g
             fl = acct.prefill_flops([P] * B, C, win, Hq, D)
-            tf = fl / (ms_call * 1e-3) / 1e12
-            res[f"W{win}"] = {"ms": ms_call, "flops": fl, "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS}
+            tf = fl / (s["median_us"] * 1e-6) / 1e12
+            res[f"W{win}"] = {"ms": s["median_us"] * 1e-3, "min_ms": s["min_us"] * 1e-3,
+                              "max_ms": s["max_us"] * 1e-3, "cold_first_call_ms": cold, "flops": fl,
+                              "TFLOPs": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
+                              "cold_frac_bf16_peak": fl / (cold * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
     return res
 
 
-def counted_traffic():
-    """HBM bytes per global-layer decode call from the committed rocprofv3
-    counter summary, or None when the decode kernel source has changed since
-    the counters were taken."""
+def counted_traffic(record="hybrid_global_traffic.json"):
+    """HBM bytes per launch of a call from a committed rocprofv3 counter
+    summary, or None when the sources it names have changed since the
+    counters were taken."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(root, "profiles", "decode_global_traffic.json")
+    path = os.path.join(root, "profiles", record)
     try:
         rec = json.load(open(path))
         h = hashlib.sha256()
@@ -543,50 +650,74 @@ def counted_traffic():
         return None
 
 
-def cpu_baseline(budget_s: float):
-    """The oracle (numpy, float64) on a bounded sample of the decode workload.
+def host_description():
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model or platform.processor() or "unknown"
 
-    Per sequence, the timed work is what one step does: encode the new token's
-    K and V rows, then the global and the window-1024 layer. The 64
-    sequences' caches are encoded once, outside the timed region; steps over
-    them are repeated until about ``budget_s`` seconds of timed work."""
+
+def cpu_baseline(budget_s: float):
+    """The oracle (numpy, float64) on a bounded sample of the hybrid block.
+
+    Per sequence, the timed work is what one block step does: encode the new
+    token's K and V rows into the three buffers' owners, then the six layers
+    (the global one over the sequence's whole context, the five window layers
+    over its last 1024 keys). Sequences' caches are generated and encoded
+    outside the timed region; sequences are taken in order until about
+    ``budget_s`` seconds of timed work."""
     import numpy as np
     from threadpoolctl import threadpool_info
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import oracle
     import synth
-    B, Hq, D, L, n = 64, 32, 128, 4096, 4
+    w = synth.HYBRID
+    Hq, D = w.Hq, w.D
+    lens = w.lens()
     t_all = time.perf_counter()
-    chunks = []
-    for c0 in range(0, B, n):
-        k = synth.normal_f32(synth.rng(2, synth.T_K, 1000 + c0), (n, L, D))
-        v = synth.normal_f32(synth.rng(2, synth.T_V, 1000 + c0), (n, L, D))
-        q = synth.q_bf16(synth.rng(2, synth.T_Q, 1000 + c0), (n, Hq, D))
-        kq, ks = oracle.quantize_rows(k[:, :-1])
-        vq, vs = oracle.quantize_rows(v[:, :-1])
-        kq = np.concatenate([kq, np.zeros((n, 1, D), np.int8)], axis=1)
-        vq = np.concatenate([vq, np.zeros((n, 1, D), np.int8)], axis=1)
-        ks = np.concatenate([ks, np.zeros((n, 1), np.float32)], axis=1)
-        vs = np.concatenate([vs, np.zeros((n, 1), np.float32)], axis=1)
-        chunks.append((k[:, -1].copy(), v[:, -1].copy(), q, kq, ks, vq, vs))
-    lens = np.full(n, L, np.int32)
-    done, t_work, steps = 0, 0.0, 0
-    while t_work < budget_s:
-        for knew, vnew, q, kq, ks, vq, vs in chunks:
-            t0 = time.perf_counter()
-            kq[:, -1], ks[:, -1] = oracle.quantize_rows(knew)
-            vq[:, -1], vs[:, -1] = oracle.quantize_rows(vnew)
-            for w in (0, 1024):
-                oracle.decode_ref(q, kq, ks, vq, vs, lens, w)
-            t_work += time.perf_counter() - t0
-            done += n
-        steps += 1
+    done, t_work, keys = 0, 0.0, 0
+    for b in range(w.B):
+        n = int(lens[b])
+        g = synth.rng(3, synth.T_K, 5000 + b)
+        bufs = {}
+        for name in ("G", "A", "Bf"):
+            rows = n if name == "G" else min(n, 1024)
+            k = synth.normal_f32(g, (1, rows, D))
+            v = synth.normal_f32(g, (1, rows, D))
+            kq, ks = oracle.quantize_rows(k)
+            vq, vs = oracle.quantize_rows(v)
+            bufs[name] = (kq, ks, vq, vs)
+        qs = [synth.q_bf16(g, (1, Hq, D)) for _ in w.layers]
+        knew, vnew = synth.normal_f32(g, (1, D)), synth.normal_f32(g, (1, D))
+        t0 = time.perf_counter()
+        for name in ("G", "A", "Bf"):             # the owners' fused append: the new token is the last row
+            kq, ks, vq, vs = bufs[name]
+            kq[0, -1], ks[0, -1] = oracle.quantize_rows(knew[0])
+            vq[0, -1], vs[0, -1] = oracle.quantize_rows(vnew[0])
+        for li, (name, win) in enumerate(w.layers):
+            kq, ks, vq, vs = bufs[name]
+            rows = kq.shape[1]
+            oracle.decode_ref(qs[li], kq, ks, vq, vs, np.array([rows], np.int32), win)
+        t_work += time.perf_counter() - t0
+        done += 1
+        keys += n + 5 * min(n, 1024)
+        if t_work >= budget_s:
+            break
     info = threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
+    blas = [{"api": i.get("internal_api"), "version": i.get("version"), "threads": i.get("num_threads")}
+            for i in info]
     return {"value": done / t_work, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{steps} decode steps of all 64 sequences (append + global layer + window-1024 layer, "
-                      f"4096 keys, 32 heads, D=128); numpy float64 oracle, {t_work:.1f} s of timed work",
-            "host_cpus": len(os.sched_getaffinity(0)), "wall_s": time.perf_counter() - t_all}
+            "sample": f"{done} of the {w.B} sequences of one hybrid block step (append + 1 global layer over "
+                      f"the whole context + 5 window-1024 layers; {keys} visible keys), numpy float64 oracle, "
+                      f"{t_work:.1f} s of timed work",
+            "cpu_model": host_description(), "host_cpus": len(os.sched_getaffinity(0)),
+            "numpy": np.__version__, "blas": blas, "wall_s": time.perf_counter() - t_all}
 
 
 def main():
@@ -609,47 +740,50 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_each_way": x.numel() * 4, "copies": 3}), file=sys.stderr)
+        del x, y
+    if args.only == "hybrid_global":
+        print(json.dumps({"extra": {"hybrid_global": bench_hybrid_global_only(torch, m, stream)}}))
+        return
+    hyb = bench_hybrid(torch, m, acct, args, stream) if args.only in (None, "hybrid") else None
     extra = {}
-    if args.only in (None, "decode"):
-        dec = bench_decode(torch, m, acct, args, stream)
-    else:
-        dec = None
     if not args.no_extra:
-        if args.only in (None, "hybrid"):
-            extra["hybrid_block"] = bench_hybrid(torch, m, acct, stream)
-        if args.only in (None, "long"):
-            extra["long_context"] = bench_long(torch, m, acct, stream)
-        if args.only in (None, "prefill"):
-            extra["prefill"] = bench_prefill(torch, m, acct, stream)
-        if args.only in (None, "paged"):
-            extra["paged"] = bench_paged(torch, m, acct, stream)
-        if args.only in (None, "q8"):
-            extra["q8"] = bench_q8(torch, m, acct, stream)
-        if args.only in (None, "prefix_cache"):
-            extra["prefix_cache"] = bench_prefix_cache(torch, m, stream)
-        if args.only in (None, "ceilings"):
-            extra["ceilings"] = bench_ceilings(torch, stream)
-    if dec is None:
+        for name, fn in (("decode_step_B64_L4096", lambda: bench_decode(torch, m, acct, stream)),
+                         ("long_context", lambda: bench_long(torch, m, acct, stream)),
+                         ("prefill", lambda: bench_prefill(torch, m, acct, stream)),
+                         ("paged", lambda: bench_paged(torch, m, acct, stream)),
+                         ("q8", lambda: bench_q8(torch, m, acct, stream)),
+                         ("prefix_cache", lambda: bench_prefix_cache(torch, m, stream)),
+                         ("ceilings", lambda: bench_ceilings(torch, stream))):
+            key = {"decode_step_B64_L4096": "decode"}.get(name, name)
+            if args.only in (None, key):
+                extra[name] = fn()
+                print(f"bench: {name} done", file=sys.stderr, flush=True)
+    if hyb is None:
         print(json.dumps({"extra": extra}))
         return
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
-    achieved = dec["global_GBps"]
+    g = hyb["global_call"]
     line = {
-        "metric": METRIC, "value": dec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
-        "steps": dec["steps_done"], "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "metric": METRIC, "value": hyb["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": hyb["steps_timed"], "warmup": args.warmup, "ms_per_step": hyb["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic",
-        "config": {"workload": "decode_B64_Hq32_D128_L4096: append + global layer + window-1024 layer "
-                               "sharing one int8 KV buffer",
-                   "B": 64, "Hq": 32, "D": 128, "seq_len": 4096, "windows": [0, 1024],
-                   "kv_rotation_copies": dec["rotation_copies"], "graph_replay": dec["graph"]},
-        "kv_read_GBps": dec["step_kv_GBps"], "kv_read_frac_hbm_peak": dec["step_kv_GBps"] / HBM_PEAK_GBPS,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": counted_traffic(),
-                     "kernel": "global layer: mqa_decode_append (decode_partition_kernel + decode_merge_kernel)",
-                     "algorithmic_bytes_per_launch": dec["global_kv_bytes"],
-                     "avg_launch_us": dec["global_call_us"]},
+        "config": {"workload": "hybrid 6-layer block decode step: 1 global + 5 window-1024 layers over 3 shared "
+                               "int8 KV buffers (G: layer 0; A: layers 1-3; B: layers 4-5), B=128 ragged "
+                               "1024..32768 keys, Hq=32, 1 KV head, D=128",
+                   "B": hyb["B"], "Hq": hyb["Hq"], "D": hyb["D"], "seq_len_range": hyb["seq_len_range"],
+                   "layers": hyb["layers"], "graph_replay": True},
+        "kv_read_GBps": hyb["kv_GBps"], "kv_read_frac_hbm_peak": hyb["kv_GBps"] / HBM_PEAK_GBPS,
+        "block_step_median_us": hyb["block_step"]["median_us"],
+        "roofline": {"bound": "hbm", "achieved": hyb["global_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": hyb["global_GBps"] / HBM_PEAK_GBPS, "traffic": counted_traffic(),
+                     "kernel": "global layer of the block: mqa_decode_append (decode_partition_kernel + "
+                               "decode_merge_kernel)",
+                     "algorithmic_bytes_per_launch": hyb["global_kv_bytes"],
+                     "avg_launch_us": g["mean_us"], "median_launch_us": g["median_us"],
+                     "launch_us_min_max": [g["min_us"], g["max_us"]], "replays": g["replays"]},
         "cpu_baseline": cpu,
+        "per_layer": hyb["per_layer"],
         "extra": extra,
     }
     print(json.dumps(line))

@@ -36,7 +36,10 @@
  *  - Device-resident lengths (seq_lens, prefix_lens, start_pos) are trusted
  *    data: kernels clamp them into the cache (and prefix_lens to
  *    max_prefix_len) so that no access leaves the buffers or the workspace,
- *    but results for out-of-range values are unspecified.
+ *    but results for out-of-range values are unspecified. Decode calls read
+ *    a seq_lens[b] larger than their max_seq_len as max_seq_len (the keys
+ *    beyond are not attended to; an appending call writes the new row at
+ *    max_seq_len - 1).
  *  - Supported shapes: head_dim D in {64, 128}; 1 <= Hq <= 64 query heads;
  *    B >= 1. Validation happens before any HIP call, so bad arguments are
  *    reported without touching the device.
@@ -56,7 +59,8 @@ typedef enum {
   MQA_ERR_NULL = 1,        /* a required pointer is NULL                        */
   MQA_ERR_SHAPE = 2,       /* a size is out of range (<= 0, or inconsistent)    */
   MQA_ERR_UNSUPPORTED = 3, /* a shape this build does not implement (D, Hq)     */
-  MQA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                  */
+  MQA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned, or a decode
+                              cache's L_cap is not a multiple of 32           */
   MQA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
   MQA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed        */
 } mqa_status;
@@ -104,7 +108,8 @@ size_t mqa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
  *   kv           host pointer to the layer's KV view (may be shared).
  *   seq_lens     int32 [B] (device): keys per sequence INCLUDING the new
  *                token, which the caller has already written to the cache.
- *   max_seq_len  host upper bound of seq_lens (sizes the launch).
+ *   max_seq_len  host upper bound of seq_lens (sizes the launch; a larger
+ *                seq_lens[b] is read as max_seq_len).
  *   window       > 0: attend to the last `window` keys (including the new
  *                token); <= 0: global.
  *   softmax_scale  multiplies q.k before the softmax (usually 1/sqrt(D)).
@@ -117,8 +122,8 @@ size_t mqa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
  * Long or many-partition contexts are split into key ranges whose partial
  * softmax states are combined by a log-sum-exp merge (exact up to rounding).
  * Layout requirements: q, k, v, out and workspace 16-byte aligned; k_scale
- * and v_scale 16-byte aligned with L_cap a multiple of 4 (scales are read
- * four keys at a time).
+ * and v_scale 16-byte aligned; L_cap a multiple of 32 (the kernels read
+ * whole 32-key tiles of a sequence's rows, and scales four keys at a time).
  * Errors: NULL, SHAPE, UNSUPPORTED, ALIGN, WORKSPACE, HIP. */
 int mqa_decode(const uint16_t* q, const mqa_kv_view* kv,
                const int32_t* seq_lens, int32_t max_seq_len, int32_t B,

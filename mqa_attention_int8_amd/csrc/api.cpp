@@ -105,7 +105,9 @@ const char* mqa_status_string(int status) {
     case MQA_ERR_NULL: return "a required pointer is NULL";
     case MQA_ERR_SHAPE: return "a size argument is out of range or inconsistent";
     case MQA_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be 64 or 128, 1 <= Hq <= 64)";
-    case MQA_ERR_ALIGN: return "a pointer is not suitably aligned (16 bytes for tensors, 4 for scales)";
+    case MQA_ERR_ALIGN:
+      return "a pointer is not suitably aligned (16 bytes for tensors, 4 for scales), or a decode call's cache "
+             "capacity L_cap is not a multiple of 32";
     case MQA_ERR_WORKSPACE: return "workspace is missing or smaller than the size the matching *_workspace_bytes() returns";
     case MQA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     default: return "unknown status";
@@ -139,8 +141,8 @@ int mqa_decode(const uint16_t* q, const mqa_kv_view* kv, const int32_t* seq_lens
   if (st != MQA_OK) return st;
   if (max_seq_len > kv->L_cap) return MQA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(out)) return MQA_ERR_ALIGN;
-  // scales are read four keys at a time
-  if ((kv->L_cap & 3) || !aligned16(kv->k_scale) || !aligned16(kv->v_scale)) return MQA_ERR_ALIGN;
+  // whole 32-key tiles per sequence; scales read four keys at a time
+  if ((kv->L_cap & 31) || !aligned16(kv->k_scale) || !aligned16(kv->v_scale)) return MQA_ERR_ALIGN;
   const mqa::DecodePlan plan = mqa::plan_decode(B, Hq, D, max_seq_len, window, device_cu_count());
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes) return MQA_ERR_WORKSPACE;
@@ -164,7 +166,7 @@ int mqa_decode_append(const uint16_t* q, const mqa_kv_cache* kv, const float* k_
   if (st != MQA_OK) return st;
   if (max_seq_len > kv->L_cap) return MQA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(out)) return MQA_ERR_ALIGN;
-  if ((kv->L_cap & 3) || !aligned16(kv->k_scale) || !aligned16(kv->v_scale)) return MQA_ERR_ALIGN;
+  if ((kv->L_cap & 31) || !aligned16(kv->k_scale) || !aligned16(kv->v_scale)) return MQA_ERR_ALIGN;
   const mqa::DecodePlan plan = mqa::plan_decode(B, Hq, D, max_seq_len, window, device_cu_count());
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes) return MQA_ERR_WORKSPACE;
@@ -280,7 +282,7 @@ int decode_q8_impl(const int8_t* q8, const float* q_scale, const mqa_kv_view& vi
   if (st != MQA_OK) return st;
   if (max_seq_len > view.L_cap) return MQA_ERR_SHAPE;
   if (!aligned16(q8) || ((uintptr_t)q_scale & 3u) || !aligned16(out)) return MQA_ERR_ALIGN;
-  if ((view.L_cap & 3) || !aligned16(view.k_scale) || !aligned16(view.v_scale)) return MQA_ERR_ALIGN;
+  if ((view.L_cap & 31) || !aligned16(view.k_scale) || !aligned16(view.v_scale)) return MQA_ERR_ALIGN;
   if (cache) {
     if (!k_new || !v_new) return MQA_ERR_NULL;
     if (((uintptr_t)k_new & 3u) || ((uintptr_t)v_new & 3u)) return MQA_ERR_ALIGN;

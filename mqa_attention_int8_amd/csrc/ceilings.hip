@@ -18,6 +18,7 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "mqa_ceilings.h"
 
 namespace mqa {
 namespace {

@@ -117,6 +117,7 @@ struct DecodeParams {
   float* ws_o;       // [B, P, Hq, D] partition outputs, normalised (natural d order)
   float2* ws_ml;     // [B, P, Hq] (offset m in log2 units, sum l of 2^(z - m))
   int32_t L_cap;
+  int32_t max_len;          // lengths are clamped to [0, max_len]: the host's max_seq_len (<= L_cap)
   int32_t Hq;
   int32_t heads_per_group;  // 16 or 32 (grid z = ceil(Hq / heads_per_group))
   int32_t window;
@@ -138,6 +139,11 @@ struct Tile {
 
 // Per-lane constant byte offsets of a tile's loads (the tile base enters as
 // the wave-uniform scalar offset, so the hot loop has no address arithmetic).
+// The range check of a buffer load covers the per-lane offset but not the
+// scalar one, so only tiles that lie wholly inside the buffer are loaded this
+// way: the cache capacity is a multiple of the 32-key tile (checked on the
+// host), every tile a work-group computes lies below the sequence length, and
+// the one loaded before the length is known is checked against the capacity.
 struct TileOffsets {
   uint32_t k;   // key base+c, bytes [g*D/4, (g+1)*D/4)
   uint32_t v;   // key base+4g, bytes [D/16*c, D/16*(c+1))
@@ -150,8 +156,8 @@ struct SeqBuffers {
 
 // Loads are issued unconditionally so the compiler can count them (a load
 // under a runtime branch makes it wait for every outstanding load); a tile
-// that does not exist is pointed past the buffer ends, where buffer loads
-// return zero without a memory access.
+// that does not exist is pointed past the buffer ends through the per-lane
+// offset, where buffer loads return zero without a memory access.
 constexpr uint32_t kNowhere = 0x80000000u;
 
 template <int D>
@@ -405,7 +411,7 @@ __device__ __forceinline__ void patch_new_row(Tile<D>& t, const int8_t* nk, cons
 // and patches the tile registers, which may hold what the cache had before.
 template <int D>
 __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D / 64], const float (&xv)[D / 64],
-                                               int8_t* scratch, int r, int g, int c, int lane, bool write,
+                                               int8_t* row_lds, int r, int g, int c, int lane, bool write,
                                                int8_t* krow, int8_t* vrow, float* ks, float* vs) {
   constexpr int E = D / 64;  // elements per lane
   float ak = 0.f, av = 0.f;
@@ -423,17 +429,17 @@ __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D /
     ck |= ((uint32_t)kv_code(xk[e], sk) & 0xffu) << (8 * e);
     cv |= ((uint32_t)kv_code(xv[e], sv) & 0xffu) << (8 * e);
   }
-  // the codes in order in the wave's LDS scratch: K at [0, D), V at [D, 2D)
+  // the codes in order in the wave's LDS row buffer: K at [0, D), V at [D, 2D)
   if constexpr (E == 2) {
-    reinterpret_cast<uint16_t*>(scratch)[lane] = (uint16_t)ck;
-    reinterpret_cast<uint16_t*>(scratch + D)[lane] = (uint16_t)cv;
+    reinterpret_cast<uint16_t*>(row_lds)[lane] = (uint16_t)ck;
+    reinterpret_cast<uint16_t*>(row_lds + D)[lane] = (uint16_t)cv;
     if (write) {
       reinterpret_cast<uint16_t*>(krow)[lane] = (uint16_t)ck;
       reinterpret_cast<uint16_t*>(vrow)[lane] = (uint16_t)cv;
     }
   } else {
-    scratch[lane] = (int8_t)ck;
-    scratch[D + lane] = (int8_t)cv;
+    row_lds[lane] = (int8_t)ck;
+    row_lds[D + lane] = (int8_t)cv;
     if (write) {
       krow[lane] = (int8_t)ck;
       vrow[lane] = (int8_t)cv;
@@ -446,7 +452,7 @@ __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D /
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes are done
   __builtin_amdgcn_wave_barrier();
   const float ns[2] = {sk, sv};
-  patch_new_row<D>(t, scratch, ns, r, g, c);
+  patch_new_row<D>(t, row_lds, ns, r, g, c);
 }
 
 // The work-group's tiles pt0 + [0, count) are handed out to its waves from an
@@ -463,7 +469,7 @@ __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D,
                                           const QOperand<D, NT, Q8>& qop, float kscale,
                                           int pt0, int count, int ia, int ib, int* next, int lane, int lo, int hi,
                                           int g, int new_tile, const float (&xk)[D / 64], const float (&xv)[D / 64],
-                                          int8_t* scratch, bool write, int8_t* krow, int8_t* vrow, float* ks,
+                                          int8_t* row_lds, bool write, int8_t* krow, int8_t* vrow, float* ks,
                                           float* vs) {
   const int c = lane & 15;
   const auto claim = [&]() {
@@ -476,14 +482,14 @@ __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D,
   while (ia < count) {
     int na = claim();
     if (ia == new_tile)
-      encode_new_row<D>(ta, xk, xv, scratch, hi - 1 - (pt0 + ia) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
+      encode_new_row<D>(ta, xk, xv, row_lds, hi - 1 - (pt0 + ia) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
     compute_tile<D, NT, Q8>(ta, st, qop, kscale, (pt0 + ia) * kTileKeys, lo, hi, g);
     ia = __builtin_amdgcn_readfirstlane(na);
     load(ta, ia);
     if (ib >= count) break;
     int nb = claim();
     if (ib == new_tile)
-      encode_new_row<D>(tb, xk, xv, scratch, hi - 1 - (pt0 + ib) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
+      encode_new_row<D>(tb, xk, xv, row_lds, hi - 1 - (pt0 + ib) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
     compute_tile<D, NT, Q8>(tb, st, qop, kscale, (pt0 + ib) * kTileKeys, lo, hi, g);
     ib = __builtin_amdgcn_readfirstlane(nb);
     load(tb, ib);
@@ -510,7 +516,7 @@ void decode_partition_kernel(DecodeParams p) {
   __shared__ float sm_m[WV][HP];
   __shared__ float sm_l[WV][HP];
   __shared__ int sm_next;  // next tile (relative to pt0) to hand out
-  __shared__ __attribute__((aligned(16))) int8_t sm_new[WV][2 * D];  // fused append: per-wave scratch
+  __shared__ __attribute__((aligned(16))) int8_t sm_new[WV][2 * D];  // fused append: per-wave row buffer
   __shared__ int sm_tab[PAGED ? kMaxTableSlice : 1];  // physical blocks of the partition's tiles
 
   const int lane = threadIdx.x & 63;
@@ -525,9 +531,9 @@ void decode_partition_kernel(DecodeParams p) {
 
   const int tpp = p.tiles_per_part;
 
-  // Contiguous layout: one buffer resource per tensor of this sequence; loads
-  // past the cache capacity return zero (rows past the valid keys are masked
-  // anyway). Paged layout: resources are made per tile (below).
+  // Contiguous layout: one buffer resource per tensor of this sequence (the
+  // rows of tiles past the length but inside the capacity are masked).
+  // Paged layout: resources are made per tile (below).
   SeqBuffers sb;
   if (!PAGED) {
     sb.k = make_rsrc(p.k + (int64_t)b * p.L_cap * D, (uint32_t)p.L_cap * D);
@@ -590,16 +596,21 @@ void decode_partition_kernel(DecodeParams p) {
   __syncthreads();
 
   // A global layer's first tile per wave does not depend on the sequence
-  // length: it is loaded before the length arrives (beyond the cache capacity
-  // buffer loads return zero; a tile past the length is never computed).
+  // length: it is loaded before the length arrives if it lies inside the
+  // cache capacity (a tile past the length is never computed).
   // A windowed layer needs the length to place its tiles. (Issuing the second
   // tile this early too measured slower: the first work-groups' loads then
   // delay the q loads of those dispatched last.)
   Tile<D> ta, tb;
-  if (!WINDOWED && !PAGED) load_tile<D>(ta, sb, off, (part * tpp + wave) * kTileKeys, wave < tpp);
+  if (!WINDOWED && !PAGED) {
+    const int t0 = part * tpp + wave;
+    load_tile<D>(ta, sb, off, t0 * kTileKeys, wave < tpp && (t0 + 1) * kTileKeys <= p.L_cap);
+  }
 
   int n = __builtin_amdgcn_readfirstlane(n_raw);  // same for the whole work-group
-  n = n < 0 ? 0 : (n > p.L_cap ? p.L_cap : n);     // paged: L_cap is the position bound
+  // A length beyond the host's max_seq_len (a caller error) is read as
+  // max_seq_len: the plan's partitions cover exactly those keys.
+  n = n < 0 ? 0 : (n > p.max_len ? p.max_len : n);
   const int lo = WINDOWED ? max(0, n - p.window) : 0;
   const int hi = n;
   const int t_begin = lo / kTileKeys;
@@ -870,7 +881,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,
                        int num_cus, int32_t block_size) {
-  DecodePlan pl{1, 1, 0, kHeadsPerGroup};
+  DecodePlan pl{1, 1, 0, kHeadsPerGroup, max_seq_len};
   // Upper bound of 32-key tiles a sequence's visible range can touch.
   int64_t ntiles;
   if (window > 0 && window < max_seq_len)
@@ -930,6 +941,7 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layo
   prm.seq_lens = seq_lens;
   prm.out = out;
   prm.L_cap = layout.table ? layout.L_cap : kv.L_cap;
+  prm.max_len = std::min(plan.max_seq_len, prm.L_cap);
   prm.Hq = Hq;
   prm.heads_per_group = plan.heads_per_group;
   prm.window = window;

@@ -29,6 +29,7 @@ struct DecodePlan {
   int num_parts;       // work-groups per sequence
   size_t ws_bytes;     // workspace for partial states (0 when num_parts == 1)
   int heads_per_group; // query heads per work-group (grid z = ceil(Hq / heads_per_group))
+  int max_seq_len;     // the host's bound on seq_lens; longer lengths are read as this
 };
 // block_size > 0: paged layout (bounds the tiles of a partition).
 DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,

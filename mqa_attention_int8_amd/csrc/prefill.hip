@@ -166,7 +166,8 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
   const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.P_max);
   const int kend = P + p.C;                            // keys [0, kend) exist
-  const int t_lo = first_needed_key(P, p.window) / kKeys;
+  const int kbeg = first_needed_key(P, p.window);      // no query of the chunk sees a key before it
+  const int t_lo = kbeg / kKeys;
   const int t_hi = (kend + kKeys - 1) / kKeys;
   if (t < t_lo || t >= t_hi) return;
   const int base = t * kKeys;
@@ -198,6 +199,9 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
   // V''^T: thread = (key group (ks, g), 4 columns). Chunk (ks, g) of row d
   // holds the 8 keys 32ks + 16(i/4) + 4g + i%4 (i = 0..7), stored at chunk
   // (4ks + g) ^ (d & 7) of the 64-key row; values fp16(v * s_v * 2^-E).
+  // Keys outside [kbeg, kend) are stored as zero: the exponent E only bounds
+  // the scales of the keys some query sees, so an unseen key's V'' could
+  // overflow fp16, and its zero weight times infinity would be NaN.
   {
     constexpr int DQ = D / 4;   // 4-column groups
     const float rE = exp2f(-p.seq_e[b]);
@@ -211,8 +215,8 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int j = base + 32 * ks + 16 * (i >> 2) + 4 * g + (i & 3);
-        ok[i] = j < kend;
-        row[i] = key_row_of<PAGED>(p, b, ok[i] ? j : kend - 1);
+        ok[i] = j >= kbeg && j < kend;
+        row[i] = key_row_of<PAGED>(p, b, j < kend ? j : kend - 1);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {

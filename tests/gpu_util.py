@@ -27,11 +27,25 @@ def dev(x: np.ndarray, dtype=None) -> torch.Tensor:
     return t.cuda()
 
 
+TILE_ROWS = 32   # decode calls take caches whose capacity is a multiple of 32 rows
+
+
+def pad_rows(a: np.ndarray, rows: int) -> np.ndarray:
+    """`a` [B, L, ...] with zero rows appended up to `rows` rows."""
+    if a.shape[1] >= rows:
+        return a
+    pad = np.zeros((a.shape[0], rows - a.shape[1]) + a.shape[2:], a.dtype)
+    return np.concatenate([a, pad], axis=1)
+
+
 class HostKV:
-    """int8 KV buffer made on the host: codes and scales from the oracle quantizer."""
+    """int8 KV buffer made on the host: codes and scales from the oracle
+    quantizer. The capacity is padded with zero rows (codes and scales) to a
+    multiple of 32; no length used with it reaches the padding."""
 
     def __init__(self, kq, ks, vq, vs):
-        self.kq, self.ks, self.vq, self.vs = kq, ks, vq, vs
+        rows = -(-kq.shape[1] // TILE_ROWS) * TILE_ROWS
+        self.kq, self.ks, self.vq, self.vs = (pad_rows(a, rows) for a in (kq, ks, vq, vs))
 
     @classmethod
     def seeded(cls, wid: int, buffer_id: int, B: int, L: int, D: int, rows=None):

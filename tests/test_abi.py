@@ -35,12 +35,12 @@ def test_every_declared_function_is_exported(lib):
 
 def test_ceilings_library_exports_its_header():
     """libmqa_ceilings.so (the benchmark's measurement kernels) loads and
-    exports what include/mqa_ceilings.h declares; only invalid arguments are
+    exports what csrc/mqa_ceilings.h declares; only invalid arguments are
     passed, which return before any launch."""
     path = os.path.join(ROOT, "mqa_attention_int8_amd", "libmqa_ceilings.so")
     assert os.path.exists(path), "build first"
     cl = ctypes.CDLL(path)
-    names = declared_functions(os.path.join(ROOT, "include", "mqa_ceilings.h"))
+    names = declared_functions(os.path.join(ROOT, "mqa_attention_int8_amd", "csrc", "mqa_ceilings.h"))
     assert set(names) == {"mqa_ceiling_stream_read", "mqa_ceiling_mfma_bf16", "mqa_ceiling_mfma_bf16_flops"}
     for n in names:
         assert hasattr(cl, n), f"{n} declared in mqa_ceilings.h but not exported"
@@ -99,6 +99,7 @@ def test_decode_validation(lib):
     assert decode(lib, Hq=65) == 3
     assert decode(lib, q=FAKE + 8) == 4
     assert decode(lib, kv=kv(L_cap=62), max_len=60) == 4     # scales read 4 keys at a time
+    assert decode(lib, kv=kv(L_cap=80), max_len=60) == 4     # whole 32-row tiles: L_cap a multiple of 32
     assert decode(lib, kv=kv(ks=FAKE + 4)) == 4
     # needs a workspace (many partitions) but none given
     assert decode(lib, kv=kv(L_cap=1 << 16), max_len=1 << 16, B=64) == 5

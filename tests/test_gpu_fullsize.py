@@ -22,7 +22,7 @@ def test_hybrid_block_full():
     B, Hq, D = w.B, w.Hq, w.D
     lens = w.lens()
     L = int(lens.max())
-    L_cap = (L + 15) // 16 * 16          # capacity: a multiple of 16 rows
+    L_cap = (L + 31) // 32 * 32          # capacity: a multiple of 32 rows
     log(f"hybrid block: B={B} lens {lens.min()}..{lens.max()}")
     # global buffer: every visible row; window buffers: only their last 1024 rows
     bufs = {"G": HostKV.seeded(w.wid, 0, B, L_cap, D, rows=[(b, 0, int(n)) for b, n in enumerate(lens)])}
@@ -56,6 +56,8 @@ def test_long_context_full():
 
 @pytest.mark.parametrize("window", [0, 1024])
 def test_prefill_full_sampled(window):
+    """Every chunk position of two sequences, and sampled positions of all
+    the others (the full-size launch: 16 sequences, XCD-grouped order)."""
     from mqa_attention_int8_amd import mqa_prefill_chunk
     w = synth.PREFILL
     B, C, P, Hq, D = w.B, w.C, w.prefix, w.Hq, w.D
@@ -66,9 +68,11 @@ def test_prefill_full_sampled(window):
     plens = np.full(B, P, np.int32)
     out = mqa_prefill_chunk(q_dev(qb), hk.to_device(), dev(plens), P, window)
     torch.cuda.synchronize()
+    full = [0, 9]
+    ref = oracle.prefill_ref(qb[full], *(a[full] for a in hk.arrays()), plens[full], window)
+    assert_prefill_close(out[full], ref, what=f"sequences {full}, every position, W={window}")
+    rest = [b for b in range(B) if b not in full]
     picks = [0, 1, 63, 64, 255, 256, 300, 510, 511]
-    seqs = [0, 5, 15]
-    sub = oracle.prefill_ref(qb[seqs], *(a[seqs] for a in hk.arrays()), plens[seqs], window,
+    sub = oracle.prefill_ref(qb[rest], *(a[rest] for a in hk.arrays()), plens[rest], window,
                              positions=picks)
-    got = out[seqs][:, picks]
-    assert_prefill_close(got, sub[:, picks], what=f"sampled positions W={window}")
+    assert_prefill_close(out[rest][:, picks], sub[:, picks], what=f"other sequences, sampled positions W={window}")

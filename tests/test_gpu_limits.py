@@ -10,18 +10,20 @@ import torch
 
 import oracle
 import synth
-from gpu_util import assert_decode_close, assert_prefill_close, dev, log, q_bits, q_dev
+from gpu_util import assert_decode_close, assert_prefill_close, dev, log, pad_rows, q_bits, q_dev
 
 pytestmark = pytest.mark.gpu
 
 BMAX = 65535
 
 
-def cache(wid, B, L, D):
-    """int8 cache [B, L, D] with every row filled: one quantizer call for all rows."""
+def cache(wid, B, L, D, cap=32):
+    """int8 cache with `cap` rows per sequence (a multiple of 32), the first L
+    of them filled: one quantizer call for all rows."""
     kq, ks = oracle.quantize_rows(synth.normal_f32(synth.rng(wid, synth.T_K), (B * L, D)))
     vq, vs = oracle.quantize_rows(synth.normal_f32(synth.rng(wid, synth.T_V), (B * L, D)))
-    return kq.reshape(B, L, D), ks.reshape(B, L), vq.reshape(B, L, D), vs.reshape(B, L)
+    return tuple(pad_rows(a, cap) for a in (kq.reshape(B, L, D), ks.reshape(B, L), vq.reshape(B, L, D),
+                                            vs.reshape(B, L)))
 
 
 def sample(B, n, seed):
@@ -45,8 +47,8 @@ def test_decode_at_the_largest_batch(window):
     ref = oracle.decode_ref_rows(qb, *arrs, lens, window, picks).reshape(len(bs), Hq, D)
     assert_decode_close(out[torch.from_numpy(bs).cuda()], ref, 1e-4, f"{len(bs)} sampled sequences")
     with pytest.raises(m.MQAError) as err:
-        m.mqa_decode(q_dev(q_bits(61, (B + 1, Hq, D))), m.KVView.empty(B + 1, L, D), dev(np.zeros(B + 1, np.int32)), L,
-                     window)
+        m.mqa_decode(q_dev(q_bits(61, (B + 1, Hq, D))), m.KVView.empty(B + 1, 32, D), dev(np.zeros(B + 1, np.int32)),
+                     L, window)
     assert err.value.code == 2  # MQA_ERR_SHAPE, before any launch
 
 

@@ -33,7 +33,7 @@ def test_two_blocks_shared_global_buffer_several_steps():
     import mqa_attention_int8_amd as m
     B, Hq, D, steps = 8, 32, 128, 3
     n0 = np.array([1, 33, 1000, 1023, 1024, 1025, 1600, 2100], np.int32)
-    L_cap = (int(n0.max()) + steps + 15) // 16 * 16  # decode reads scales in 16-byte groups: a multiple of 4 rows
+    L_cap = (int(n0.max()) + steps + 31) // 32 * 32  # decode takes whole 32-row tiles: a multiple of 32 rows
     log(f"schedule: 2 blocks x 6 layers, B={B} Hq={Hq} D={D} lens {n0.tolist()} + {steps} steps, L_cap={L_cap}")
 
     # the cache before step 0 holds rows [0, n0 - 1); window buffers only their visible part
