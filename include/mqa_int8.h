@@ -131,6 +131,26 @@ int mqa_decode(const uint16_t* q, const mqa_kv_view* kv,
                float* out, void* workspace, size_t workspace_bytes,
                void* stream);
 
+/* mqa_decode_noalloc - mqa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): no workspace argument, and the call allocates nothing.
+ * The partition states that mqa_decode keeps in its workspace go to a static
+ * device array of the library, 8 MiB per GPU (MQA_NOALLOC_SCRATCH_BYTES),
+ * held by each GPU the library runs on until the process ends. Its address is
+ * looked up on the first call on each device. Every call on a GPU shares that
+ * GPU's array: calls that may overlap on one GPU (several streams, several
+ * host threads) race and must be serialised by the caller. Nothing in the
+ * array needs clearing: each call writes every state it later reads.
+ * Arguments, layout and results as mqa_decode.
+ * Errors: as mqa_decode; MQA_ERR_WORKSPACE when the call would need more than
+ * MQA_NOALLOC_SCRATCH_BYTES (mqa_decode_workspace_bytes of the same
+ * arguments tells), MQA_ERR_HIP when the array's address cannot be found. */
+#define MQA_NOALLOC_SCRATCH_BYTES (8u << 20)
+int mqa_decode_noalloc(const uint16_t* q, const mqa_kv_view* kv,
+                       const int32_t* seq_lens, int32_t max_seq_len, int32_t B,
+                       int32_t Hq, int32_t D, int32_t window, float softmax_scale,
+                       float* out, void* stream);
+
 /* Writable view of ONE KV buffer, for the call that appends to it. Same
  * layout as mqa_kv_view. */
 typedef struct {

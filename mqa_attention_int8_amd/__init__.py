@@ -4,7 +4,7 @@ The compute lives in libmqa_int8.so (hand-written HIP for gfx950, C ABI in
 include/mqa_int8.h); ``binding`` marshals torch tensors to it.
 """
 from .binding import (KVView, MQAError, append_kv, kv_quantize_int8, load_library,  # noqa: F401
-                      mqa_decode, mqa_decode_append, mqa_decode_workspace_bytes, mqa_prefill_chunk,
+                      mqa_decode, mqa_decode_noalloc, mqa_decode_append, mqa_decode_workspace_bytes, mqa_prefill_chunk,
                       mqa_status_string, default_softmax_scale, library_path,
                       decode_workspace, mqa_prefill_workspace_bytes, prefill_workspace,
                       PagedKV, kv_quantize_int8_paged, mqa_decode_paged, mqa_decode_append_paged,

@@ -74,6 +74,9 @@ def load_library() -> ctypes.CDLL:
         lib.mqa_decode.argtypes = [vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32, f32,
                                    vp, vp, ctypes.c_size_t, vp]
         lib.mqa_decode.restype = ctypes.c_int
+        lib.mqa_decode_noalloc.argtypes = [vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32, f32,
+                                           vp, vp]
+        lib.mqa_decode_noalloc.restype = ctypes.c_int
         lib.mqa_decode_append.argtypes = [vp, ctypes.POINTER(mqa_kv_cache), vp, vp, vp, i32, i32, i32, i32, i32,
                                           f32, vp, vp, ctypes.c_size_t, vp]
         lib.mqa_decode_append.restype = ctypes.c_int
@@ -245,6 +248,27 @@ def mqa_decode(q: torch.Tensor, kv: KVView, seq_lens: torch.Tensor, max_seq_len:
     _check(lib.mqa_decode(_ptr(q), ctypes.byref(view), _ptr(seq_lens), int(max_seq_len), B, Hq, D,
                           int(window), scale, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
            "mqa_decode")
+    return out
+
+
+def mqa_decode_noalloc(q: torch.Tensor, kv: KVView, seq_lens: torch.Tensor, max_seq_len: int, window: int,
+                       softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """mqa_decode with the partition states in the library's static device
+    array (no workspace; the C call allocates nothing). Pass `out` to keep
+    the binding itself from allocating the output."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q", 3)
+    _need(seq_lens, torch.int32, "seq_lens", 1)
+    B, Hq, D = (int(x) for x in q.shape)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out", 3)
+    scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
+    view = kv.c_view()
+    _check(lib.mqa_decode_noalloc(_ptr(q), ctypes.byref(view), _ptr(seq_lens), int(max_seq_len), B, Hq, D,
+                                  int(window), scale, _ptr(out), _stream(stream)),
+           "mqa_decode_noalloc")
     return out
 
 

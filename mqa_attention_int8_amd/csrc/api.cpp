@@ -152,6 +152,28 @@ int mqa_decode(const uint16_t* q, const mqa_kv_view* kv, const int32_t* seq_lens
                             plan, static_cast<hipStream_t>(stream));
 }
 
+int mqa_decode_noalloc(const uint16_t* q, const mqa_kv_view* kv, const int32_t* seq_lens, int32_t max_seq_len,
+                       int32_t B, int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
+                       void* stream) {
+  if (!q || !kv || !seq_lens || !out) return MQA_ERR_NULL;
+  int st = check_decode_shape(B, Hq, D, max_seq_len);
+  if (st != MQA_OK) return st;
+  st = check_kv(kv, D);
+  if (st != MQA_OK) return st;
+  if (max_seq_len > kv->L_cap) return MQA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(out)) return MQA_ERR_ALIGN;
+  if ((kv->L_cap & 31) || !aligned16(kv->k_scale) || !aligned16(kv->v_scale)) return MQA_ERR_ALIGN;
+  const mqa::DecodePlan plan = mqa::plan_decode(B, Hq, D, max_seq_len, window, device_cu_count());
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    if (plan.ws_bytes > mqa::kStaticScratchBytes) return MQA_ERR_WORKSPACE;
+    ws = mqa::static_scratch();
+    if (ws == nullptr) return MQA_ERR_HIP;
+  }
+  return mqa::launch_decode(q, *kv, mqa::KVLayout{}, seq_lens, B, Hq, D, window, softmax_scale, out, ws, plan,
+                            static_cast<hipStream_t>(stream));
+}
+
 int mqa_decode_append(const uint16_t* q, const mqa_kv_cache* kv, const float* k_new, const float* v_new,
                       const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq, int32_t D,
                       int32_t window, float softmax_scale, float* out, void* workspace,

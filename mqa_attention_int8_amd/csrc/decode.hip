@@ -49,6 +49,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -914,6 +916,39 @@ DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, in
     pl.ws_bytes = align_up(slots * sizeof(float2), 256) + align_up(slots * (size_t)D * sizeof(float), 256);
   }
   return pl;
+}
+
+// Device memory of the allocation-free decode entry point: the partition
+// states of one call (each GPU holds its own copy for the life of the
+// process). In host code `scratch` names a host-side stand-in, never the
+// device array: its device address is looked up once per device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+void* static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+  if (ptr == nullptr) {
+    // the current device is `dev`: the address returned is its copy's
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_addr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
 }
 
 int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layout, const int32_t* seq_lens,

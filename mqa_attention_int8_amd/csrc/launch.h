@@ -59,6 +59,12 @@ struct QueryInt8 {
   const float* scale;
 };
 
+// Allocation-free decode: the partition states live in a static device array
+// of kStaticScratchBytes per GPU; static_scratch() returns the current
+// device's copy (looked up once per device), or nullptr if that fails.
+constexpr size_t kStaticScratchBytes = MQA_NOALLOC_SCRATCH_BYTES;
+void* static_scratch();
+
 // q == nullptr with q8 set: the int8-query variant.
 int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layout, const int32_t* seq_lens,
                   int32_t B, int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,

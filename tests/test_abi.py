@@ -108,6 +108,29 @@ def test_decode_validation(lib):
     assert decode(lib, kv=kv(L_cap=1 << 26), max_len=64, D=64) == 2
 
 
+def test_noalloc_decode_rejects_before_any_launch(lib):
+    """The allocation-free decode validates like mqa_decode and rejects calls
+    whose partition states would not fit in its static 8 MiB array; every
+    case returns before any HIP call."""
+    def call(**kw):
+        a = dict(q=FAKE, kv=kv(), seq=FAKE, max_len=64, B=2, Hq=8, D=128, W=0, scale=0.1, out=FAKE)
+        a.update(kw)
+        v = a["kv"]
+        return lib.mqa_decode_noalloc(a["q"], ctypes.byref(v) if v is not None else None, a["seq"], a["max_len"],
+                                      a["B"], a["Hq"], a["D"], a["W"], a["scale"], a["out"], None)
+    assert call(q=None) == 1
+    assert call(kv=None) == 1
+    assert call(B=0) == 2
+    assert call(max_len=65) == 2
+    assert call(D=96) == 3
+    assert call(kv=kv(L_cap=80), max_len=60) == 4
+    import mqa_attention_int8_amd as m
+    # 127 sequences x 64 heads x 65536 keys: two partitions per sequence, 8,453,120 bytes of states
+    need = m.mqa_decode_workspace_bytes(127, 64, 128, 65536, 0)
+    assert need > (8 << 20)
+    assert call(kv=kv(L_cap=65536), max_len=65536, B=127, Hq=64) == 5
+
+
 def test_quantize_validation(lib):
     assert lib.kv_quantize_int8(None, FAKE, FAKE, FAKE, 1, 1, 128, 8, None) == 1
     assert lib.kv_quantize_int8(FAKE, FAKE, FAKE, FAKE, 1, 9, 128, 8, None) == 2
