@@ -137,16 +137,24 @@ def bench_hybrid(torch, m, acct, args, stream):
     knew = torch.randn((B, D), generator=gen, device="cuda")
     vnew = torch.randn((B, D), generator=gen, device="cuda")
     out = torch.empty((B, Hq, D), device="cuda")
-    ws = torch.zeros(max(m.mqa_decode_workspace_bytes(B, Hq, D, L, win) for _, win in w.layers) + 16,
+    ws = torch.zeros(max(max(m.mqa_decode_workspace_bytes(B, Hq, D, L, win),
+                             m.mqa_decode_ragged_workspace_bytes(B, Hq, D, L, win)) for _, win in w.layers) + 16,
                      dtype=torch.uint8, device="cuda")
     owners = {}
     for li, (name, _) in enumerate(w.layers):
         owners.setdefault(name, li)
 
     def layer(li):
+        # the global layer's lengths differ widely: it runs the balanced (ragged) plan; the window
+        # layers see at most 1024 keys per sequence and keep the whole-window plan
         name, win = w.layers[li]
         kv = bufs[name]
-        if owners[name] == li:             # first layer of a sharing group writes the token (fused)
+        if win <= 0:
+            if owners[name] == li:             # first layer of a sharing group writes the token (fused)
+                m.mqa_decode_append_ragged(q[li], kv, knew, vnew, seq_lens, L, win, out=out, workspace=ws)
+            else:
+                m.mqa_decode_ragged(q[li], kv, seq_lens, L, win, out=out, workspace=ws)
+        elif owners[name] == li:
             m.mqa_decode_append(q[li], kv, knew, vnew, seq_lens, L, win, out=out, workspace=ws)
         else:
             m.mqa_decode(q[li], kv, seq_lens, L, win, out=out, workspace=ws)
@@ -234,10 +242,10 @@ def bench_hybrid_global_only(torch, m, stream, calls=8):
     knew = torch.randn((B, D), generator=gen, device="cuda")
     vnew = torch.randn((B, D), generator=gen, device="cuda")
     out = torch.empty((B, Hq, D), device="cuda")
-    ws = m.decode_workspace(B, Hq, D, L, 0)
+    ws = m.ragged_workspace(B, Hq, D, L, 0)
     with torch.cuda.stream(stream):
         for _ in range(calls):
-            m.mqa_decode_append(q, kv, knew, vnew, seq_lens, L, 0, out=out, workspace=ws)
+            m.mqa_decode_append_ragged(q, kv, knew, vnew, seq_lens, L, 0, out=out, workspace=ws)
         torch.cuda.synchronize()
     return {"workload": w.name + " global layer", "calls": calls}
 
@@ -777,8 +785,8 @@ def main():
         "block_step_median_us": hyb["block_step"]["median_us"],
         "roofline": {"bound": "hbm", "achieved": hyb["global_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": hyb["global_GBps"] / HBM_PEAK_GBPS, "traffic": counted_traffic(),
-                     "kernel": "global layer of the block: mqa_decode_append (decode_partition_kernel + "
-                               "decode_merge_kernel)",
+                     "kernel": "global layer of the block: mqa_decode_append_ragged (decode_plan_kernel + "
+                               "decode_partition_kernel + decode_merge_kernel)",
                      "algorithmic_bytes_per_launch": hyb["global_kv_bytes"],
                      "avg_launch_us": g["mean_us"], "median_launch_us": g["median_us"],
                      "launch_us_min_max": [g["min_us"], g["max_us"]], "replays": g["replays"]},

@@ -181,6 +181,44 @@ int mqa_decode_append(const uint16_t* q, const mqa_kv_cache* kv, const float* k_
                       float softmax_scale, float* out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace mqa_decode_ragged / mqa_decode_append_ragged need
+ * (pure host function; 0 for invalid arguments). */
+size_t mqa_decode_ragged_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
+                                         int32_t max_seq_len, int32_t window);
+
+/* mqa_decode_ragged - mqa_decode for batches whose lengths differ widely.
+ * [9c1h.cn page "秘訣1": the global layers (one in six) attend to each
+ * dialog's whole history; "秘訣2": dialogs are long and of very different
+ * lengths.] mqa_decode splits every sequence into the same number of key
+ * ranges (from max_seq_len alone), so the compute units holding the longest
+ * sequences finish last. Here a small planning kernel on the same stream
+ * reads seq_lens and cuts the visible 32-key tiles of all sequences, taken in
+ * order as one flat range, into equal ranges, one per work-group; a range
+ * may end one sequence and start the next, and the partial softmax states of
+ * every sequence are merged as in mqa_decode. A sliding window short enough
+ * for mqa_decode's whole-window plan uses that plan (no planning kernel).
+ * Results equal mqa_decode's up to the order of the floating-point sums.
+ *   workspace  at least mqa_decode_ragged_workspace_bytes() bytes: the plan
+ *              and the partial states (no initialisation needed).
+ * Other arguments, layout and errors as mqa_decode; also MQA_ERR_SHAPE when
+ * B * ceil(max_seq_len / 32) reaches 2^31 (the plan counts tiles in 32-bit
+ * integers). */
+int mqa_decode_ragged(const uint16_t* q, const mqa_kv_view* kv,
+                      const int32_t* seq_lens, int32_t max_seq_len, int32_t B,
+                      int32_t Hq, int32_t D, int32_t window, float softmax_scale,
+                      float* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* mqa_decode_append_ragged - mqa_decode_append with the balanced plan of
+ * mqa_decode_ragged (the owner layer of a buffer: appends the new token's K
+ * and V, then attends). Arguments as mqa_decode_append; workspace as
+ * mqa_decode_ragged. */
+int mqa_decode_append_ragged(const uint16_t* q, const mqa_kv_cache* kv, const float* k_new,
+                             const float* v_new, const int32_t* seq_lens, int32_t max_seq_len,
+                             int32_t B, int32_t Hq, int32_t D, int32_t window,
+                             float softmax_scale, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace mqa_prefill_chunk needs (pure host function;
  * 0 for invalid arguments). */
 size_t mqa_prefill_workspace_bytes(int32_t B, int32_t C, int32_t D,

@@ -80,6 +80,14 @@ def load_library() -> ctypes.CDLL:
         lib.mqa_decode_append.argtypes = [vp, ctypes.POINTER(mqa_kv_cache), vp, vp, vp, i32, i32, i32, i32, i32,
                                           f32, vp, vp, ctypes.c_size_t, vp]
         lib.mqa_decode_append.restype = ctypes.c_int
+        lib.mqa_decode_ragged_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.mqa_decode_ragged_workspace_bytes.restype = ctypes.c_size_t
+        lib.mqa_decode_ragged.argtypes = [vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32, f32,
+                                          vp, vp, ctypes.c_size_t, vp]
+        lib.mqa_decode_ragged.restype = ctypes.c_int
+        lib.mqa_decode_append_ragged.argtypes = [vp, ctypes.POINTER(mqa_kv_cache), vp, vp, vp, i32, i32, i32, i32,
+                                                 i32, f32, vp, vp, ctypes.c_size_t, vp]
+        lib.mqa_decode_append_ragged.restype = ctypes.c_int
         lib.mqa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.mqa_prefill_workspace_bytes.restype = ctypes.c_size_t
         lib.mqa_prefill_chunk.argtypes = [vp, ctypes.POINTER(mqa_kv_view), vp, i32, i32, i32, i32, i32,
@@ -299,6 +307,69 @@ def mqa_decode_append(q: torch.Tensor, kv: KVView, k_new: torch.Tensor, v_new: t
                                  int(max_seq_len), B, Hq, D, int(window), scale, _ptr(out), _ptr(workspace),
                                  ws_bytes, _stream(stream)),
            "mqa_decode_append")
+    return out
+
+
+def mqa_decode_ragged_workspace_bytes(B: int, Hq: int, D: int, max_seq_len: int, window: int) -> int:
+    return int(load_library().mqa_decode_ragged_workspace_bytes(B, Hq, D, max_seq_len, window))
+
+
+def ragged_workspace(B: int, Hq: int, D: int, max_seq_len: int, window: int, device="cuda"):
+    """A workspace for mqa_decode_ragged / mqa_decode_append_ragged (None when none is needed)."""
+    need = mqa_decode_ragged_workspace_bytes(B, Hq, D, max_seq_len, window)
+    if need == 0:
+        return None
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+def _ragged_ws(B, Hq, D, max_seq_len, window, workspace, device):
+    need = mqa_decode_ragged_workspace_bytes(B, Hq, D, max_seq_len, window)
+    if workspace is None and need > 0:
+        workspace = ragged_workspace(B, Hq, D, max_seq_len, window, device)
+    return workspace, (0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def mqa_decode_ragged(q: torch.Tensor, kv: KVView, seq_lens: torch.Tensor, max_seq_len: int, window: int,
+                      softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mqa_decode with work balanced over the compute units from the actual lengths."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q", 3)
+    _need(seq_lens, torch.int32, "seq_lens", 1)
+    B, Hq, D = (int(x) for x in q.shape)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out", 3)
+    workspace, ws_bytes = _ragged_ws(B, Hq, D, max_seq_len, window, workspace, q.device)
+    scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
+    view = kv.c_view()
+    _check(lib.mqa_decode_ragged(_ptr(q), ctypes.byref(view), _ptr(seq_lens), int(max_seq_len), B, Hq, D,
+                                 int(window), scale, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
+           "mqa_decode_ragged")
+    return out
+
+
+def mqa_decode_append_ragged(q: torch.Tensor, kv: KVView, k_new: torch.Tensor, v_new: torch.Tensor,
+                             seq_lens: torch.Tensor, max_seq_len: int, window: int,
+                             softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mqa_decode_append with work balanced over the compute units from the actual lengths."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q", 3)
+    _need(seq_lens, torch.int32, "seq_lens", 1)
+    B, Hq, D = (int(x) for x in q.shape)
+    _need(k_new, torch.float32, "k_new", 2)
+    _need(v_new, torch.float32, "v_new", 2)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out", 3)
+    workspace, ws_bytes = _ragged_ws(B, Hq, D, max_seq_len, window, workspace, q.device)
+    scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
+    cache = kv.c_cache()
+    _check(lib.mqa_decode_append_ragged(_ptr(q), ctypes.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
+                                        int(max_seq_len), B, Hq, D, int(window), scale, _ptr(out),
+                                        _ptr(workspace), ws_bytes, _stream(stream)),
+           "mqa_decode_append_ragged")
     return out
 
 

@@ -199,6 +199,66 @@ int mqa_decode_append(const uint16_t* q, const mqa_kv_cache* kv, const float* k_
                             plan, static_cast<hipStream_t>(stream), &rows);
 }
 
+namespace {
+// The balanced planner counts tiles in 32-bit integers.
+bool ragged_tiles_fit(int32_t B, int32_t max_seq_len) {
+  return (int64_t)B * (((int64_t)max_seq_len + 31) / 32 + 1) < ((int64_t)1 << 31);
+}
+
+int decode_ragged_impl(const uint16_t* q, const mqa_kv_view& view, const mqa_kv_cache* cache, const float* k_new,
+                       const float* v_new, const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq,
+                       int32_t D, int32_t window, float softmax_scale, float* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!q || !seq_lens || !out) return MQA_ERR_NULL;
+  int st = check_decode_shape(B, Hq, D, max_seq_len);
+  if (st != MQA_OK) return st;
+  st = check_kv(&view, D);
+  if (st != MQA_OK) return st;
+  if (max_seq_len > view.L_cap || !ragged_tiles_fit(B, max_seq_len)) return MQA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(out)) return MQA_ERR_ALIGN;
+  if ((view.L_cap & 31) || !aligned16(view.k_scale) || !aligned16(view.v_scale)) return MQA_ERR_ALIGN;
+  if (cache) {
+    if (!k_new || !v_new) return MQA_ERR_NULL;
+    if (((uintptr_t)k_new & 3u) || ((uintptr_t)v_new & 3u)) return MQA_ERR_ALIGN;
+  }
+  const mqa::DecodePlan plan = mqa::plan_decode_ragged(B, Hq, D, max_seq_len, window, device_cu_count());
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_ALIGN;
+  }
+  if (cache) {
+    const mqa::AppendRows rows{k_new, v_new, cache->k, cache->v, cache->k_scale, cache->v_scale};
+    return mqa::launch_decode(q, view, mqa::KVLayout{}, seq_lens, B, Hq, D, window, softmax_scale, out, workspace,
+                              plan, static_cast<hipStream_t>(stream), &rows);
+  }
+  return mqa::launch_decode(q, view, mqa::KVLayout{}, seq_lens, B, Hq, D, window, softmax_scale, out, workspace,
+                            plan, static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+size_t mqa_decode_ragged_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window) {
+  if (check_decode_shape(B, Hq, D, max_seq_len) != MQA_OK || !ragged_tiles_fit(B, max_seq_len)) return 0;
+  return mqa::plan_decode_ragged(B, Hq, D, max_seq_len, window, device_cu_count()).ws_bytes;
+}
+
+int mqa_decode_ragged(const uint16_t* q, const mqa_kv_view* kv, const int32_t* seq_lens, int32_t max_seq_len,
+                      int32_t B, int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kv) return MQA_ERR_NULL;
+  return decode_ragged_impl(q, *kv, nullptr, nullptr, nullptr, seq_lens, max_seq_len, B, Hq, D, window,
+                            softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int mqa_decode_append_ragged(const uint16_t* q, const mqa_kv_cache* kv, const float* k_new, const float* v_new,
+                             const int32_t* seq_lens, int32_t max_seq_len, int32_t B, int32_t Hq, int32_t D,
+                             int32_t window, float softmax_scale, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!kv) return MQA_ERR_NULL;
+  const mqa_kv_view view{kv->k, kv->v, kv->k_scale, kv->v_scale, kv->L_cap};
+  return decode_ragged_impl(q, view, kv, k_new, v_new, seq_lens, max_seq_len, B, Hq, D, window, softmax_scale,
+                            out, workspace, workspace_bytes, stream);
+}
+
 size_t mqa_prefill_workspace_bytes(int32_t B, int32_t C, int32_t D, int32_t max_prefix_len) {
   if (B <= 0 || C <= 0 || max_prefix_len < 0 || !supported_d(D)) return 0;
   return mqa::prefill_workspace_bytes(B, C, D, max_prefix_len);

@@ -116,8 +116,14 @@ struct DecodeParams {
   int32_t table_len;
   int32_t log2_bs;
   int32_t num_blocks;
-  float* ws_o;       // [B, P, Hq, D] partition outputs, normalised (natural d order)
-  float2* ws_ml;     // [B, P, Hq] (offset m in log2 units, sum l of 2^(z - m))
+  float* ws_o;       // [slots, Hq, D] partition outputs, normalised (natural d order)
+  float2* ws_ml;     // [slots, Hq] (offset m in log2 units, sum l of 2^(z - m))
+  // Balanced plan of a ragged batch (written by decode_plan_kernel): header
+  // {chunk c, total tiles T, pieces}, then per work-group the piece {sequence,
+  // first tile, tiles, whole sequence?}, then per sequence {first piece,
+  // pieces}.
+  const int32_t* plan;
+  int32_t B;
   int32_t L_cap;
   int32_t max_len;          // lengths are clamped to [0, max_len]: the host's max_seq_len (<= L_cap)
   int32_t Hq;
@@ -502,9 +508,12 @@ __device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D,
 // tiles then depend on the sequence length); otherwise to all of them.
 // PAGED: the cache is a block pool addressed through p.table.
 // Q8: int8 queries (p.q8, p.q_scale) and int8 MFMA for Q K^T.
-template <int D, int NT, bool WINDOWED, bool PAGED, bool Q8>
+// RAGGED: balanced plan (one piece of a sequence per work-group, see
+// DecodeParams and decode_plan_kernel).
+template <int D, int NT, bool WINDOWED, bool PAGED, bool Q8, bool RAGGED>
 __global__ __launch_bounds__(64 * kWavesPerWG) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partition_kernel(DecodeParams p) {
+  static_assert(!RAGGED || (!PAGED && !Q8), "balanced plans serve contiguous bf16-query calls");
   static_assert(NT == 1 || NT == 2, "a work-group serves at most 32 heads");
   constexpr int WV = kWavesPerWG;
   constexpr int NTHR = 64 * WV;
@@ -525,14 +534,21 @@ void decode_partition_kernel(DecodeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4;
   const int c = lane & 15;
-  const int b = blockIdx.y;
-  const int part = blockIdx.x;
   const int Hq = p.Hq;                     // heads of the layer (row stride of q and out)
   const int h0 = p.heads_per_group * (int)blockIdx.z;   // first head of this group
   const int Hg = min(Hq - h0, min(p.heads_per_group, NT * 16));    // heads of this group
 
-  const int tpp = p.tiles_per_part;
+  TileOffsets off;
+  off.k = (uint32_t)(c * D + g * (D / 4));
+  off.v = (uint32_t)(4 * g * D + (D / 16) * c);
+  off.s = (uint32_t)(16 * g);
 
+  // One segment: sequence b, its visible tiles [seg_lo, seg_lo + seg_len)
+  // (relative to the first visible tile; tiles past the visible range are
+  // dropped). The states go to partial-state slot `slot`, or straight to the
+  // output when the segment is the whole sequence (`direct`).
+  const auto segment = [&](const int b, const int seg_lo, const int seg_len, const int64_t slot,
+                           const bool direct) {
   // Contiguous layout: one buffer resource per tensor of this sequence (the
   // rows of tiles past the length but inside the capacity are masked).
   // Paged layout: resources are made per tile (below).
@@ -543,11 +559,6 @@ void decode_partition_kernel(DecodeParams p) {
     sb.ks = make_rsrc(p.ks + (int64_t)b * p.L_cap, (uint32_t)p.L_cap * 4);
     sb.vs = make_rsrc(p.vs + (int64_t)b * p.L_cap, (uint32_t)p.L_cap * 4);
   }
-  TileOffsets off;
-  off.k = (uint32_t)(c * D + g * (D / 4));
-  off.v = (uint32_t)(4 * g * D + (D / 16) * c);
-  off.s = (uint32_t)(16 * g);
-
   // Loads go out first: the sequence length, the q rows this lane needs and
   // the new K/V row elements (fused append). A compute unit's vector memory
   // requests are served in order, so every wave issues these before any wave
@@ -605,21 +616,22 @@ void decode_partition_kernel(DecodeParams p) {
   // delay the q loads of those dispatched last.)
   Tile<D> ta, tb;
   if (!WINDOWED && !PAGED) {
-    const int t0 = part * tpp + wave;
-    load_tile<D>(ta, sb, off, t0 * kTileKeys, wave < tpp && (t0 + 1) * kTileKeys <= p.L_cap);
+    const int t0 = seg_lo + wave;
+    load_tile<D>(ta, sb, off, t0 * kTileKeys, wave < seg_len && (t0 + 1) * kTileKeys <= p.L_cap);
   }
 
   int n = __builtin_amdgcn_readfirstlane(n_raw);  // same for the whole work-group
   // A length beyond the host's max_seq_len (a caller error) is read as
-  // max_seq_len: the plan's partitions cover exactly those keys.
+  // max_seq_len: the plan's partitions cover exactly those keys (the
+  // balanced planner clamps the same way).
   n = n < 0 ? 0 : (n > p.max_len ? p.max_len : n);
   const int lo = WINDOWED ? max(0, n - p.window) : 0;
   const int hi = n;
   const int t_begin = lo / kTileKeys;
   const int t_end = hi > lo ? (hi + kTileKeys - 1) / kTileKeys : t_begin;
-  const int pt0 = t_begin + part * tpp;
-  const int pt1 = min(pt0 + tpp, t_end);
-  const int count = pt1 - pt0;  // tiles of this partition (may be <= 0)
+  const int pt0 = t_begin + seg_lo;
+  const int pt1 = min(pt0 + seg_len, t_end);
+  const int count = pt1 - pt0;  // tiles of this segment (may be <= 0)
   // Fused append: the wave that draws the tile holding row n - 1 encodes it.
   const int new_tile = (appending && n > 0) ? (n - 1) / kTileKeys - pt0 : -1;  // outside [0, count): none here
 
@@ -729,7 +741,6 @@ void decode_partition_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  const int64_t slot = (int64_t)b * p.num_parts + part;
   for (int job = threadIdx.x; job < NT * 256; job += NTHR) {
     const int nt = job >> 8;
     const int gq = (job >> 6) & 3;
@@ -762,7 +773,7 @@ void decode_partition_kernel(DecodeParams p) {
     }
     if (h < Hg) {
       float* dst;
-      if (p.num_parts == 1) {
+      if (direct) {
         dst = p.out + ((int64_t)b * Hq + h0 + h) * D + d0;
       } else {
         dst = p.ws_o + (slot * Hq + h0 + h) * D + d0;
@@ -772,6 +783,20 @@ void decode_partition_kernel(DecodeParams p) {
       for (int u = 0; u < DPL; u += 4)
         *reinterpret_cast<f32x4*>(dst + u) = f32x4{o[u], o[u + 1], o[u + 2], o[u + 3]};
     }
+  }
+  };
+
+  if constexpr (!RAGGED) {
+    const int part = blockIdx.x, tpp = p.tiles_per_part;
+    segment(blockIdx.y, part * tpp, tpp, (int64_t)blockIdx.y * p.num_parts + part, p.num_parts == 1);
+  } else {
+    // one piece of the balanced plan per work-group; work-groups past the
+    // last piece have nothing to do
+    const int4 piece = *reinterpret_cast<const int4*>(p.plan + 4 + 4 * blockIdx.x);
+    const int b = __builtin_amdgcn_readfirstlane(piece.x);
+    if (b >= p.B) return;
+    segment(b, __builtin_amdgcn_readfirstlane(piece.y), __builtin_amdgcn_readfirstlane(piece.z),
+            (int64_t)blockIdx.x, piece.w != 0);
   }
 }
 
@@ -788,7 +813,8 @@ constexpr int kMergeMaxSlices = 4;
 template <int D>
 __global__ __launch_bounds__(256 * kMergeMaxSlices) void decode_merge_kernel(const float* __restrict__ ws_o,
                                                                              const float2* __restrict__ ws_ml,
-                                                                             float* __restrict__ out, int Hq, int P) {
+                                                                             float* __restrict__ out, int Hq, int P,
+                                                                             const int32_t* __restrict__ plan, int G) {
   constexpr int D4 = D / 4;
   constexpr int HPB = 256 / D4;  // heads per block
   __shared__ f32x4 s_acc[kMergeMaxSlices - 1][256];
@@ -800,8 +826,18 @@ __global__ __launch_bounds__(256 * kMergeMaxSlices) void decode_merge_kernel(con
   const int h = blockIdx.x * HPB + t / D4;
   const int d0 = 4 * (t % D4);
   const bool live_h = h < Hq;
-  const float2* ml = ws_ml + (int64_t)b * P * Hq + h;
-  const float* wo = ws_o + ((int64_t)b * P * Hq + h) * D + d0;
+  // States of sequence b: slots s0 .. s0 + P - 1. Balanced plan: the
+  // sequence's pieces wrote consecutive slots; a sequence in one piece was
+  // written to the output directly, one with no visible key gets zeros.
+  int64_t s0 = (int64_t)b * P;
+  if (plan != nullptr) {
+    const int2 sq = *reinterpret_cast<const int2*>(plan + 4 + 4 * G + 2 * b);
+    if (sq.y == 1) return;
+    s0 = sq.x;
+    P = sq.y;
+  }
+  const float2* ml = ws_ml + s0 * Hq + h;
+  const float* wo = ws_o + (s0 * Hq + h) * D + d0;
   float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int q0 = slice; q0 < P; q0 += 8 * S) {
@@ -851,28 +887,120 @@ __global__ __launch_bounds__(256 * kMergeMaxSlices) void decode_merge_kernel(con
   *reinterpret_cast<f32x4*>(out + ((int64_t)b * Hq + h) * D + d0) = acc * inv;
 }
 
-template <int D, int NT, bool PAGED, bool Q8>
-void launch_partitions(const DecodeParams& prm, int B, hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// Balanced plan of a ragged batch (one work-group of kPlanThreads threads).
+// With T the visible 32-key tiles of all sequences and G the work-groups
+// that fill the chip once, c = max(8, ceil(T / G)); sequence b (t_b visible
+// tiles) is cut into n_b = ceil(t_b / c) pieces of near-equal size, so no
+// piece exceeds c tiles whatever the lengths, and there are at most G + B
+// pieces, one work-group each, in sequence order (the pieces of a sequence
+// use consecutive partial-state slots). Written: header {c, T, pieces, 0};
+// per work-group of the launch (NW of them) its piece {b, first tile, tiles,
+// n_b == 1}, or b = B when it has none; per sequence {first piece, n_b}.
+// Lengths are clamped exactly as the attention kernel clamps them.
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+constexpr int kMinChunk = kWavesPerWG;  // at least one tile per wave
+
+__device__ __forceinline__ int visible_tiles(int n, int window, int max_len) {
+  n = n < 0 ? 0 : (n > max_len ? max_len : n);
+  const int lo = window > 0 ? max(0, n - window) : 0;
+  const int t_begin = lo / kTileKeys;
+  const int t_end = n > lo ? (n + kTileKeys - 1) / kTileKeys : t_begin;
+  return t_end - t_begin;
+}
+
+// Inclusive prefix sum over the block; `total` receives the block's sum.
+__device__ __forceinline__ int block_inclusive_sum(int v, int* sm, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) sm[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    int x = lane < kPlanThreads / 64 ? sm[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < kPlanThreads / 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane < kPlanThreads / 64) sm[lane] = x;
+  }
+  __syncthreads();
+  const int add = w > 0 ? sm[w - 1] : 0;
+  total = sm[kPlanThreads / 64 - 1];
+  __syncthreads();  // sm is reused by the next call
+  return v + add;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t* __restrict__ seq_lens,
+                                                                   int32_t* __restrict__ plan, int B, int window,
+                                                                   int max_len, int G, int NW) {
+  __shared__ int sm[kPlanThreads / 64];
+  const int tid = threadIdx.x;
+  int part = 0;
+  for (int b = tid; b < B; b += kPlanThreads) part += visible_tiles(seq_lens[b], window, max_len);
+  int total;
+  (void)block_inclusive_sum(part, sm, total);
+  const int chunk = max(kMinChunk, (total + G - 1) / G);
+  int32_t* pieces = plan + 4;
+  int32_t* seqs = plan + 4 + 4 * NW;
+  int carry = 0;
+  for (int base = 0; base < B; base += kPlanThreads) {
+    const int b = base + tid;
+    const int t = b < B ? visible_tiles(seq_lens[b], window, max_len) : 0;
+    const int n = (t + chunk - 1) / chunk;
+    int tot;
+    const int first = carry + block_inclusive_sum(n, sm, tot) - n;
+    if (b < B) {
+      *reinterpret_cast<int2*>(seqs + 2 * b) = make_int2(first, n);
+      for (int k = 0; k < n; ++k) {
+        const int lo = (int)((int64_t)k * t / n), hi = (int)((int64_t)(k + 1) * t / n);
+        *reinterpret_cast<int4*>(pieces + 4 * (first + k)) = make_int4(b, lo, hi - lo, n == 1);
+      }
+    }
+    carry += tot;
+  }
+  for (int w = carry + tid; w < NW; w += kPlanThreads)
+    *reinterpret_cast<int4*>(pieces + 4 * w) = make_int4(B, 0, 0, 0);
+  if (tid == 0) {
+    plan[0] = chunk;
+    plan[1] = total;
+    plan[2] = carry;
+    plan[3] = 0;
+  }
+}
+
+template <int D, int NT, bool PAGED, bool Q8, bool RAGGED>
+void launch_partitions(const DecodeParams& prm, int B, int G, hipStream_t stream) {
   const dim3 block(64 * kWavesPerWG);
-  const dim3 grid(prm.num_parts, B, (prm.Hq + prm.heads_per_group - 1) / prm.heads_per_group);
+  const int groups = (prm.Hq + prm.heads_per_group - 1) / prm.heads_per_group;
+  // balanced plan: one work-group per piece, at most G + B pieces
+  const dim3 grid = RAGGED ? dim3(G + B, 1, groups) : dim3(prm.num_parts, B, groups);
   if (prm.window > 0)
-    hipLaunchKernelGGL((decode_partition_kernel<D, NT, true, PAGED, Q8>), grid, block, 0, stream, prm);
+    hipLaunchKernelGGL((decode_partition_kernel<D, NT, true, PAGED, Q8, RAGGED>), grid, block, 0, stream, prm);
   else
-    hipLaunchKernelGGL((decode_partition_kernel<D, NT, false, PAGED, Q8>), grid, block, 0, stream, prm);
+    hipLaunchKernelGGL((decode_partition_kernel<D, NT, false, PAGED, Q8, RAGGED>), grid, block, 0, stream, prm);
 }
 
 template <int D>
-void launch_by_heads(const DecodeParams& prm, int B, hipStream_t stream) {
-  // int8 queries are served on contiguous buffers only
-  const bool paged = prm.table != nullptr, q8 = prm.q8 != nullptr;
+void launch_by_heads(const DecodeParams& prm, int B, int G, hipStream_t stream) {
+  // int8 queries are served on contiguous buffers only; balanced plans on
+  // contiguous buffers with bf16 queries
+  const bool paged = prm.table != nullptr, q8 = prm.q8 != nullptr, ragged = prm.plan != nullptr;
   if (prm.Hq <= 16 || prm.heads_per_group <= 16) {
-    if (q8) launch_partitions<D, 1, false, true>(prm, B, stream);
-    else if (paged) launch_partitions<D, 1, true, false>(prm, B, stream);
-    else launch_partitions<D, 1, false, false>(prm, B, stream);
+    if (q8) launch_partitions<D, 1, false, true, false>(prm, B, G, stream);
+    else if (paged) launch_partitions<D, 1, true, false, false>(prm, B, G, stream);
+    else if (ragged) launch_partitions<D, 1, false, false, true>(prm, B, G, stream);
+    else launch_partitions<D, 1, false, false, false>(prm, B, G, stream);
   } else {
-    if (q8) launch_partitions<D, 2, false, true>(prm, B, stream);
-    else if (paged) launch_partitions<D, 2, true, false>(prm, B, stream);
-    else launch_partitions<D, 2, false, false>(prm, B, stream);
+    if (q8) launch_partitions<D, 2, false, true, false>(prm, B, G, stream);
+    else if (paged) launch_partitions<D, 2, true, false, false>(prm, B, G, stream);
+    else if (ragged) launch_partitions<D, 2, false, false, true>(prm, B, G, stream);
+    else launch_partitions<D, 2, false, false, false>(prm, B, G, stream);
   }
 }
 
@@ -883,7 +1011,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,
                        int num_cus, int32_t block_size) {
-  DecodePlan pl{1, 1, 0, kHeadsPerGroup, max_seq_len};
+  DecodePlan pl{1, 1, 0, kHeadsPerGroup, max_seq_len, 0};
   // Upper bound of 32-key tiles a sequence's visible range can touch.
   int64_t ntiles;
   if (window > 0 && window < max_seq_len)
@@ -915,6 +1043,26 @@ DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, in
     const size_t slots = (size_t)B * (size_t)parts * (size_t)Hq;
     pl.ws_bytes = align_up(slots * sizeof(float2), 256) + align_up(slots * (size_t)D * sizeof(float), 256);
   }
+  return pl;
+}
+
+DecodePlan plan_decode_ragged(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,
+                              int num_cus) {
+  // Sliding windows short enough for the whole-range plan keep it: every
+  // sequence's work is then at most one window.
+  DecodePlan pl = plan_decode(B, Hq, D, max_seq_len, window, num_cus);
+  if (pl.heads_per_group == 16) return pl;
+  const int64_t groups = (Hq + kHeadsPerGroup - 1) / kHeadsPerGroup;
+  const int64_t target = num_cus > 0 ? num_cus : 256;
+  const int64_t G = std::max<int64_t>(1, target / groups);
+  pl.ragged_groups = (int)G;
+  pl.heads_per_group = kHeadsPerGroup;
+  pl.tiles_per_part = 0;
+  pl.num_parts = 0;
+  const size_t plan_words = 4 + 4 * ((size_t)G + (size_t)B) + 2 * (size_t)B;
+  const size_t slots = ((size_t)G + (size_t)B) * (size_t)Hq;
+  pl.ws_bytes = align_up(plan_words * sizeof(int32_t), 256) + align_up(slots * sizeof(float2), 256) +
+                align_up(slots * (size_t)D * sizeof(float), 256);
   return pl;
 }
 
@@ -985,7 +1133,24 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layo
   prm.scale_log2 = softmax_scale * 1.4426950408889634f;
   prm.ws_o = nullptr;
   prm.ws_ml = nullptr;
-  if (plan.num_parts > 1) {
+  prm.plan = nullptr;
+  prm.B = B;
+  const int G = plan.ragged_groups;
+  if (G > 0) {
+    // balanced plan: plan area, then the states of G + B slots
+    const size_t plan_words = 4 + 4 * ((size_t)G + (size_t)B) + 2 * (size_t)B;
+    const size_t slots = ((size_t)G + (size_t)B) * (size_t)Hq;
+    char* ws = static_cast<char*>(workspace);
+    int32_t* plan_area = reinterpret_cast<int32_t*>(ws);
+    ws += align_up(plan_words * sizeof(int32_t), 256);
+    prm.ws_ml = reinterpret_cast<float2*>(ws);
+    ws += align_up(slots * sizeof(float2), 256);
+    prm.ws_o = reinterpret_cast<float*>(ws);
+    prm.plan = plan_area;
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, plan_area, B, window,
+                       prm.max_len, G, G + B);
+    if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
+  } else if (plan.num_parts > 1) {
     const size_t slots = (size_t)B * (size_t)plan.num_parts * (size_t)Hq;
     char* ws = static_cast<char*>(workspace);
     prm.ws_ml = reinterpret_cast<float2*>(ws);
@@ -993,21 +1158,21 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layo
     prm.ws_o = reinterpret_cast<float*>(ws);
   }
   if (D == 128)
-    launch_by_heads<128>(prm, B, stream);
+    launch_by_heads<128>(prm, B, G, stream);
   else
-    launch_by_heads<64>(prm, B, stream);
+    launch_by_heads<64>(prm, B, G, stream);
   if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
-  if (plan.num_parts > 1) {
+  if (G > 0 || plan.num_parts > 1) {
     const int hpb = 256 / (D / 4);
     const dim3 grid((Hq + hpb - 1) / hpb, B);
-    const int slices = std::min(kMergeMaxSlices, (plan.num_parts + 7) / 8);
+    const int slices = G > 0 ? kMergeMaxSlices : std::min(kMergeMaxSlices, (plan.num_parts + 7) / 8);
     const dim3 block(256 * slices);
     if (D == 128)
       hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, stream, prm.ws_o, prm.ws_ml, out, Hq,
-                         plan.num_parts);
+                         plan.num_parts, prm.plan, G + B);
     else
       hipLaunchKernelGGL(decode_merge_kernel<64>, grid, block, 0, stream, prm.ws_o, prm.ws_ml, out, Hq,
-                         plan.num_parts);
+                         plan.num_parts, prm.plan, G + B);
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
   }
   return MQA_OK;

@@ -30,10 +30,17 @@ struct DecodePlan {
   size_t ws_bytes;     // workspace for partial states (0 when num_parts == 1)
   int heads_per_group; // query heads per work-group (grid z = ceil(Hq / heads_per_group))
   int max_seq_len;     // the host's bound on seq_lens; longer lengths are read as this
+  int ragged_groups;   // > 0: balanced plan of a ragged batch with this many work-groups per head group
 };
 // block_size > 0: paged layout (bounds the tiles of a partition).
 DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,
                        int num_cus, int32_t block_size = 0);
+// Balanced plan for a batch of ragged lengths (contiguous buffers, bf16
+// queries): a planner kernel splits the visible tiles of all sequences into
+// equal ranges per work-group; windows short enough for the whole-range plan
+// keep it (ragged_groups == 0 then).
+DecodePlan plan_decode_ragged(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,
+                              int num_cus);
 
 int launch_quantize(const float* src, int8_t* dst, float* dst_scale, const int32_t* start_pos,
                     int32_t B, int32_t T, int32_t D, int32_t L_cap, hipStream_t stream);

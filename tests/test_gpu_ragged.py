@@ -1,0 +1,104 @@
+"""mqa_decode_ragged / mqa_decode_append_ragged (a planning kernel splits the
+visible tiles of all sequences into pieces of at most ceil(T / G) tiles, one
+work-group each) against the oracle, and against mqa_decode on the same
+inputs (the same arithmetic summed in another order)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import HostKV, assert_decode_close, dev, log, q_bits, q_dev
+
+pytestmark = pytest.mark.gpu
+
+T_KNEW, T_VNEW = synth.T_KNEW, synth.T_VNEW
+
+
+def ragged_case(wid, B, L, Hq, D, lens, window, what, max_len=None, fill=None):
+    import mqa_attention_int8_amd as m
+    lens = np.asarray(lens, np.int32)
+    max_len = int(lens.max()) if max_len is None else max_len
+    log(f"ragged {what}: B={B} L={L} Hq={Hq} D={D} W={window} lens {int(lens.min())}..{int(lens.max())} "
+        f"workspace {m.mqa_decode_ragged_workspace_bytes(B, Hq, D, max_len, window)} B")
+    rows = fill if fill is not None else [(b, 0, int(min(n, L))) for b, n in enumerate(lens)]
+    hk = HostKV.seeded(wid, 0, B, L, D, rows=rows)
+    kv = hk.to_device()
+    qb = q_bits(wid, (B, Hq, D))
+    q, seq = q_dev(qb), dev(lens)
+    out = m.mqa_decode_ragged(q, kv, seq, max_len, window)
+    torch.cuda.synchronize()
+    ref = oracle.decode_ref(qb, *hk.arrays(), np.minimum(lens, max_len), window)
+    assert_decode_close(out, ref, 1e-4, f"{what}: ragged vs oracle")
+    uni = m.mqa_decode(q, kv, seq, max_len, window)
+    torch.cuda.synchronize()
+    assert_decode_close(out, uni.cpu().numpy().astype(np.float64), 2e-5, f"{what}: ragged vs mqa_decode")
+
+
+def test_hybrid_global_layer_full():
+    """The hybrid block's global layer: 128 sequences of 1024..32768 keys."""
+    w = synth.HYBRID
+    lens = w.lens()
+    L = (int(lens.max()) + 31) // 32 * 32
+    ragged_case(w.wid, w.B, L, w.Hq, w.D, lens, 0, "hybrid global layer")
+
+
+@pytest.mark.parametrize("window", [0, 100, 5000])
+def test_mixed_lengths(window):
+    lens = [0, 1, 31, 32, 33, 64, 1000, 4096, 20000, 7, 12345, 0, 3, 9000, 15000, 2]
+    ragged_case(97, len(lens), 20000, 32, 128, lens, window, f"mixed W{window}")
+
+
+def test_many_short_sequences():
+    """1000 sequences of 0..300 keys: most are a single piece written directly."""
+    lens = synth.ragged_lens(synth.rng(98, synth.T_LENS), 1000, 0, 300)
+    ragged_case(98, 1000, 320, 8, 64, lens, 0, "1000 short")
+
+
+@pytest.mark.parametrize("Hq,D", [(64, 128), (8, 64), (20, 128)])
+def test_head_counts(Hq, D):
+    lens = synth.ragged_lens(synth.rng(99, synth.T_LENS, Hq), 12, 1, 9000)
+    ragged_case(99, 12, 9024, Hq, D, lens, 0, f"Hq{Hq} D{D}")
+
+
+def test_uniform_lengths_and_one_sequence():
+    ragged_case(100, 64, 4096, 32, 128, [4096] * 64, 0, "uniform B64 L4096")
+    ragged_case(101, 1, 40000, 32, 128, [40000], 0, "one sequence of 40000")
+
+
+def test_lengths_beyond_max_seq_len_are_clamped():
+    """A seq_lens entry above max_seq_len is read as max_seq_len (the planner
+    and the attention kernel clamp alike)."""
+    ragged_case(102, 4, 2048, 32, 128, [3000, 100, 2000, 5000], 0, "clamped", max_len=1500)
+
+
+def test_append_ragged_hybrid_global():
+    """The owner layer of the global buffer: the new token's K and V are
+    encoded into row n - 1 (bit-exact) and attended to in the same call."""
+    import mqa_attention_int8_amd as m
+    w = synth.HYBRID
+    B, Hq, D = w.B, w.Hq, w.D
+    lens = w.lens()
+    L = (int(lens.max()) + 31) // 32 * 32
+    log(f"append ragged hybrid global: B={B}")
+    hk = HostKV.seeded(w.wid, 3, B, L, D, rows=[(b, 0, int(n) - 1) for b, n in enumerate(lens)])
+    knew = synth.normal_f32(synth.rng(w.wid, T_KNEW, 3), (B, D))
+    vnew = synth.normal_f32(synth.rng(w.wid, T_VNEW, 3), (B, D))
+    kq_new, ks_new = oracle.quantize_rows(knew)
+    vq_new, vs_new = oracle.quantize_rows(vnew)
+    exp = [a.copy() for a in hk.arrays()]
+    for b in range(B):
+        n = int(lens[b])
+        exp[0][b, n - 1], exp[1][b, n - 1] = kq_new[b], ks_new[b]
+        exp[2][b, n - 1], exp[3][b, n - 1] = vq_new[b], vs_new[b]
+    qb = q_bits(w.wid, (B, Hq, D), 3)
+    kv = hk.to_device()
+    out = m.mqa_decode_append_ragged(q_dev(qb), kv, dev(knew), dev(vnew), dev(lens), int(lens.max()), 0)
+    torch.cuda.synchronize()
+    for name, got, want in (("k", kv.k, exp[0]), ("k_scale", kv.k_scale, exp[1]), ("v", kv.v, exp[2]),
+                            ("v_scale", kv.v_scale, exp[3])):
+        g = got.cpu().numpy()
+        assert g.view(np.uint8).tobytes() == np.ascontiguousarray(want).view(np.uint8).tobytes(), \
+            f"cache {name} differs from the oracle encoding"
+    ref = oracle.decode_ref(qb, *exp, lens, 0)
+    assert_decode_close(out, ref, 1e-4, "append ragged vs oracle")
