@@ -88,43 +88,47 @@ __device__ __forceinline__ uint32_t cvt_pk_f16(float a, float b) {
 }
 
 // int8 -> fp16, exact, one instruction per byte: an SDWA convert sign-extends
-// the selected byte of `w` and writes the low half (upper half cleared) or the
-// high half (low half kept) of the result. hipcc does not form these itself.
-#define MQA_F16_LO(SEL)                                                                        \
-  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_" #SEL \
-      : "=v"(d) : "v"(w))
-#define MQA_F16_HI(SEL)                                                                             \
-  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_" #SEL \
-      : "+v"(d) : "v"(w))
-template <int SEL>
-__device__ __forceinline__ uint32_t f16_lo_of_byte(uint32_t w) {
-  uint32_t d;
-  if constexpr (SEL == 0) MQA_F16_LO(0);
-  else if constexpr (SEL == 1) MQA_F16_LO(1);
-  else if constexpr (SEL == 2) MQA_F16_LO(2);
-  else MQA_F16_LO(3);
-  return d;
-}
-template <int SEL>
-__device__ __forceinline__ uint32_t f16_hi_of_byte(uint32_t d, uint32_t w) {
-  if constexpr (SEL == 0) MQA_F16_HI(0);
-  else if constexpr (SEL == 1) MQA_F16_HI(1);
-  else if constexpr (SEL == 2) MQA_F16_HI(2);
-  else MQA_F16_HI(3);
-  return d;
-}
-#undef MQA_F16_LO
-#undef MQA_F16_HI
+// the selected byte of a word and writes the low half (upper half cleared) or
+// the high half (low half kept) of the result. hipcc does not form these
+// itself, so they are written as inline asm, and the compiler's hazard
+// tracking does not see asm as vector ALU work: each block below therefore
+// keeps its own wait states. A half written through dst_sel is read by the
+// next instruction only after one wait state (the four low halves come first,
+// so every high-half write is at least three instructions after the low half
+// it keeps), and a vector ALU result may feed an MFMA source only after two;
+// each block ends with three (s_nop 2) before anything can read its results.
 
-// Byte SEL of w0 and of w1 as a packed fp16 pair {w0, w1}.
+// One MFMA operand of four fp16 pairs: pair i = {byte SEL of w[2i], byte SEL
+// of w[2i + 1]}.
 template <int SEL>
-__device__ __forceinline__ uint32_t f16_pair_of_bytes(uint32_t w0, uint32_t w1) {
-  return f16_hi_of_byte<SEL>(f16_lo_of_byte<SEL>(w0), w1);
+__device__ __forceinline__ u32x4 f16_pairs_of_bytes(const uint32_t (&w)[8]) {
+  uint32_t d0, d1, d2, d3;
+#define MQA_LO(D, W) "v_cvt_f16_i16_sdwa " D ", sext(" W ") dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%12\n\t"
+#define MQA_HI(D, W) "v_cvt_f16_i16_sdwa " D ", sext(" W ") dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%12\n\t"
+  asm(MQA_LO("%0", "%4") MQA_LO("%1", "%6") MQA_LO("%2", "%8") MQA_LO("%3", "%10")
+      MQA_HI("%0", "%5") MQA_HI("%1", "%7") MQA_HI("%2", "%9") MQA_HI("%3", "%11") "s_nop 2"
+      : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]), "i"(SEL));
+  return u32x4{d0, d1, d2, d3};
 }
-// Four int8 codes (one word) -> four fp16 values (two words), in order.
-__device__ __forceinline__ u32x2 i8x4_to_f16(uint32_t w) {
-  return u32x2{f16_hi_of_byte<1>(f16_lo_of_byte<0>(w), w), f16_hi_of_byte<3>(f16_lo_of_byte<2>(w), w)};
+// Eight int8 codes (two words) -> eight fp16 values (one MFMA operand), in order.
+__device__ __forceinline__ u32x4 i8x8_to_f16(uint32_t w0, uint32_t w1) {
+  uint32_t d0, d1, d2, d3;
+  asm("v_cvt_f16_i16_sdwa %0, sext(%4) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+      "v_cvt_f16_i16_sdwa %1, sext(%4) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+      "v_cvt_f16_i16_sdwa %2, sext(%5) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+      "v_cvt_f16_i16_sdwa %3, sext(%5) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+      "v_cvt_f16_i16_sdwa %0, sext(%4) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1\n\t"
+      "v_cvt_f16_i16_sdwa %1, sext(%4) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3\n\t"
+      "v_cvt_f16_i16_sdwa %2, sext(%5) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1\n\t"
+      "v_cvt_f16_i16_sdwa %3, sext(%5) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3\n\t"
+      "s_nop 2"
+      : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+      : "v"(w0), "v"(w1));
+  return u32x4{d0, d1, d2, d3};
 }
+#undef MQA_LO
+#undef MQA_HI
 
 // Split two fp32 values into fp16 hi + lo parts, both rounded to nearest
 // even: hi = fp16(x), lo = fp16(x - hi) with the difference formed exactly in
@@ -134,8 +138,14 @@ __device__ __forceinline__ u32x2 i8x4_to_f16(uint32_t w) {
 __device__ __forceinline__ u32x2 split_f16(float a, float b) {
   const uint32_t hi = cvt_pk_f16(a, b);
   uint32_t lo;
-  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(hi), "v"(a));
-  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(lo) : "v"(hi), "v"(b));
+  // asm, so its wait states are its own (as for the conversions above): one
+  // after the low-half write, three before the result may feed an MFMA
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
+      "s_nop 0\n\t"
+      "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "s_nop 2"
+      : "=&v"(lo)
+      : "v"(hi), "v"(a), "v"(b));
   return u32x2{hi, lo};
 }
 

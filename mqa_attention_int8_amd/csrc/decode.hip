@@ -145,64 +145,152 @@ struct Tile {
   f32x4 vs[2];
 };
 
-// Per-lane constant byte offsets of a tile's loads (the tile base enters as
-// the wave-uniform scalar offset, so the hot loop has no address arithmetic).
-// The range check of a buffer load covers the per-lane offset but not the
-// scalar one, so only tiles that lie wholly inside the buffer are loaded this
-// way: the cache capacity is a multiple of the 32-key tile (checked on the
-// host), every tile a work-group computes lies below the sequence length, and
-// the one loaded before the length is known is checked against the capacity.
-struct TileOffsets {
-  uint32_t k;   // key base+c, bytes [g*D/4, (g+1)*D/4)
-  uint32_t v;   // key base+4g, bytes [D/16*c, D/16*(c+1))
-  uint32_t s;   // scales of keys base+4g .. base+4g+3
-};
-
 struct SeqBuffers {
   __amdgpu_buffer_rsrc_t k, v, ks, vs;
+};
+
+// A tile is staged in LDS: each wave has two slots of its own, filled by
+// direct-to-LDS buffer loads (no registers held while in flight). Every load
+// instruction reads 1 KB of K or V rows contiguous in memory (a wave reading
+// 16 scattered bytes per lane per row measured ~30% slower on the same
+// bytes); within each row the 16-byte chunks are stored XOR-swizzled by the
+// row index, so that the reads that put the rows into the MFMA operand
+// layout are free of bank conflicts. Slot layout: K rows [32][D], V rows
+// [32][D], then the 32 K scales and the 32 V scales (each stored twice, lane
+// l holding the scale of key l % 32).
+template <int D>
+struct Slot {
+  static constexpr int kCh = D / 16;              // 16-byte chunks per row
+  static constexpr int kKV = kTileKeys * D;       // bytes of K (and of V) per tile
+  static constexpr int kOffV = kKV;
+  static constexpr int kOffKs = 2 * kKV;
+  static constexpr int kOffVs = 2 * kKV + 256;
+  static constexpr int kBytes = 2 * kKV + 512;
+  static constexpr int kDma = 2 * (kKV / 1024) + 2;  // load instructions per tile
 };
 
 // Loads are issued unconditionally so the compiler can count them (a load
 // under a runtime branch makes it wait for every outstanding load); a tile
 // that does not exist is pointed past the buffer ends through the per-lane
-// offset, where buffer loads return zero without a memory access.
+// offset, where buffer loads return zero without a memory access (and the
+// slot receives zeros).
 constexpr uint32_t kNowhere = 0x80000000u;
 
+// Per-lane offsets of the staging loads: lane l of a 1 KB load takes chunk
+// (l % kCh) ^ (row % kCh) of row l / kCh of that kilobyte, so that LDS chunk
+// position p holds chunk (p % kCh) ^ (row % kCh) of row p / kCh.
 template <int D>
-__device__ __forceinline__ void load_tile(Tile<D>& t, const SeqBuffers& sb, const TileOffsets& off0,
-                                          int base, bool exists) {
-  TileOffsets off = off0;
-  if (!exists) {
-    off.k = kNowhere;
-    off.v = kNowhere;
-    off.s = kNowhere;
-    base = 0;
+__device__ __forceinline__ uint32_t stage_lane_offset(int lane) {
+  constexpr int CH = Slot<D>::kCh;
+  const int r = lane / CH;
+  return (uint32_t)(r * D + (((lane % CH) ^ (r % CH)) * 16));
+}
+
+// Direct-to-LDS buffer loads: each lane's 16 (or 4) bytes land at
+// lds + 16 * lane (or 4 * lane); the 16-byte form is non-temporal.
+__device__ __forceinline__ void lds_load16_nt(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, kCachePolicyNT);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, soff, 0, 0);
+}
+
+// Issue the loads of the tile whose first row is `base` (scalar offset) into
+// `slot`. The tile base enters as the scalar offset, which the range check of
+// a buffer load does not cover: only tiles wholly inside the buffer exist.
+template <int D>
+__device__ __forceinline__ void stage_tile(char* slot, const SeqBuffers& sb, uint32_t lane_kv, uint32_t lane_sc,
+                                           int base, bool exists) {
+  const uint32_t vk = exists ? lane_kv : kNowhere;
+  const uint32_t vs = exists ? lane_sc : kNowhere;
+  const uint32_t kv_s = __builtin_amdgcn_readfirstlane(exists ? (uint32_t)base * D : 0u);
+  const uint32_t sc_s = __builtin_amdgcn_readfirstlane(exists ? (uint32_t)base * 4 : 0u);
+  // K and V are read once per call: non-temporal loads (measured faster)
+#pragma unroll
+  for (int j = 0; j < Slot<D>::kKV / 1024; ++j) lds_load16_nt(sb.k, slot + j * 1024, vk + j * 1024, kv_s);
+#pragma unroll
+  for (int j = 0; j < Slot<D>::kKV / 1024; ++j) lds_load16_nt(sb.v, slot + Slot<D>::kOffV + j * 1024, vk + j * 1024, kv_s);
+  lds_load4(sb.ks, slot + Slot<D>::kOffKs, vs, sc_s);
+  lds_load4(sb.vs, slot + Slot<D>::kOffVs, vs, sc_s);
+}
+
+// The staged tile in the register layout the MFMAs take (see Tile). The
+// reads are written out in one asm block that waits for them: the compiler
+// cannot tell which slot a staging load in flight writes, and before a read
+// of either slot it would wait for all of them (the caller waits for the
+// slot's own loads). Lane (g, c) reads K rows c and 16 + c (chunks
+// g*KV4 + w, swizzled by the row), V rows 16(i/4) + 4g + i%4 at byte
+// c*D/16, and the scales of keys 16hf + 4g .. +3.
+template <int D>
+__device__ __forceinline__ void read_slot(Tile<D>& t, const char* slot, int g, int c) {
+  constexpr int CH = Slot<D>::kCh;
+  constexpr int HALF = 16 * D;  // bytes of 16 rows: rows r and r + 16 share the swizzle
+  const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)slot);
+  uint32_t ak[Tile<D>::KV4], av[4];
+#pragma unroll
+  for (int w = 0; w < Tile<D>::KV4; ++w) ak[w] = base + (c * CH + ((g * Tile<D>::KV4 + w) ^ (c % CH))) * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * g + i;
+    av[i] = base + Slot<D>::kOffV + r * D + (((D == 128 ? c >> 1 : c >> 2) ^ (r % CH)) * 16) +
+            (D == 128 ? (c & 1) * 8 : (c & 3) * 4);
   }
-  // scalar offsets of the tile's first row (base is wave-uniform). K and V
-  // are read once per call: non-temporal loads (measured faster); the
-  // scales keep the default policy.
-  const uint32_t kv_s = __builtin_amdgcn_readfirstlane((uint32_t)base * D);
-  const uint32_t sc_s = __builtin_amdgcn_readfirstlane((uint32_t)base * 4);
+  const uint32_t as = base + Slot<D>::kOffKs + 16 * g;
+  static_assert(Slot<D>::kOffVs - Slot<D>::kOffKs == 256, "scale layout");
+  if constexpr (D == 128) {
+    u32x2 v[8];
+    asm volatile(
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %16 offset:2048\n\t"
+        "ds_read_b128 %2, %17\n\t"
+        "ds_read_b128 %3, %17 offset:2048\n\t"
+        "ds_read_b64 %4, %18\n\t"
+        "ds_read_b64 %5, %19\n\t"
+        "ds_read_b64 %6, %20\n\t"
+        "ds_read_b64 %7, %21\n\t"
+        "ds_read_b64 %8, %18 offset:2048\n\t"
+        "ds_read_b64 %9, %19 offset:2048\n\t"
+        "ds_read_b64 %10, %20 offset:2048\n\t"
+        "ds_read_b64 %11, %21 offset:2048\n\t"
+        "ds_read_b128 %12, %22\n\t"
+        "ds_read_b128 %13, %22 offset:64\n\t"
+        "ds_read_b128 %14, %22 offset:256\n\t"
+        "ds_read_b128 %15, %22 offset:320\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t.k[0][0]), "=&v"(t.k[1][0]), "=&v"(t.k[0][1]), "=&v"(t.k[1][1]), "=&v"(v[0]), "=&v"(v[1]),
+          "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(t.ks[0]),
+          "=&v"(t.ks[1]), "=&v"(t.vs[0]), "=&v"(t.vs[1])
+        : "v"(ak[0]), "v"(ak[1]), "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]), "v"(as));
+    static_assert(HALF == 2048, "offsets above assume D = 128");
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int w = 0; w < Tile<D>::KV4; ++w) t.k[hf][w] = buf_load16_nt(sb.k, off.k + hf * 16 * D + 16 * w, kv_s);
-  // key slot i: key base + 16(i/4) + 4g + i%4
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t o = off.v + (16 * (i >> 2) + (i & 3)) * D;
-    if constexpr (Tile<D>::VW == 2) {
-      const u32x2 x = buf_load8_nt(sb.v, o, kv_s);
-      t.v[i][0] = x[0];
-      t.v[i][1] = x[1];
-    } else {
-      t.v[i][0] = buf_load4_nt(sb.v, o, kv_s);
+    for (int i = 0; i < 8; ++i) {
+      t.v[i][0] = v[i][0];
+      t.v[i][1] = v[i][1];
     }
-  }
+  } else {
+    static_assert(D == 64 && HALF == 1024, "offsets below assume D = 64");
+    uint32_t v[8];
+    asm volatile(
+        "ds_read_b128 %0, %14\n\t"
+        "ds_read_b128 %1, %14 offset:1024\n\t"
+        "ds_read_b32 %2, %15\n\t"
+        "ds_read_b32 %3, %16\n\t"
+        "ds_read_b32 %4, %17\n\t"
+        "ds_read_b32 %5, %18\n\t"
+        "ds_read_b32 %6, %15 offset:1024\n\t"
+        "ds_read_b32 %7, %16 offset:1024\n\t"
+        "ds_read_b32 %8, %17 offset:1024\n\t"
+        "ds_read_b32 %9, %18 offset:1024\n\t"
+        "ds_read_b128 %10, %19\n\t"
+        "ds_read_b128 %11, %19 offset:64\n\t"
+        "ds_read_b128 %12, %19 offset:256\n\t"
+        "ds_read_b128 %13, %19 offset:320\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t.k[0][0]), "=&v"(t.k[1][0]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]),
+          "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(t.ks[0]), "=&v"(t.ks[1]), "=&v"(t.vs[0]), "=&v"(t.vs[1])
+        : "v"(ak[0]), "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]), "v"(as));
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    t.ks[hf] = __builtin_bit_cast(f32x4, buf_load16(sb.ks, off.s + 64 * hf, sc_s));
-    t.vs[hf] = __builtin_bit_cast(f32x4, buf_load16(sb.vs, off.s + 64 * hf, sc_s));
+    for (int i = 0; i < 8; ++i) t.v[i][0] = v[i];
   }
 }
 
@@ -275,7 +363,7 @@ __device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const u32x4 w = cur.k[hf][kk >> 1];
-        const f16x8 kop = as_f16x8(cat(i8x4_to_f16(w[2 * (kk & 1)]), i8x4_to_f16(w[2 * (kk & 1) + 1])));
+        const f16x8 kop = as_f16x8(i8x8_to_f16(w[2 * (kk & 1)], w[2 * (kk & 1) + 1]));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) s[hf][nt] = mfma16_f16(kop, qop.h[nt][kk], s[hf][nt]);
       }
@@ -368,10 +456,10 @@ __device__ __forceinline__ void compute_tile(Tile<D>& cur, WaveState<D, NT>& st,
   // ---- O^T += V^T P''^T -------------------------------------------------------
   static_for<0, DPL>([&](auto MT) {
     constexpr int mt = decltype(MT)::value;
-    u32x4 a;
+    uint32_t vw[8];
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) a[i >> 1] = f16_pair_of_bytes<mt & 3>(cur.v[i][mt >> 2], cur.v[i + 1][mt >> 2]);
-    const f16x8 vop = as_f16x8(a);
+    for (int i = 0; i < 8; ++i) vw[i] = cur.v[i][mt >> 2];
+    const f16x8 vop = as_f16x8(f16_pairs_of_bytes<mt & 3>(vw));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       st.oacc[mt][nt] = mfma16_f16(vop, phi[nt], st.oacc[mt][nt]);
@@ -463,44 +551,65 @@ __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D /
   patch_new_row<D>(t, row_lds, ns, r, g, c);
 }
 
+// Atomic add on an LDS counter, returning the old value. Written out so the
+// compiler does not order it behind the staging loads in flight (it cannot
+// tell the counter from the slots those loads write, and would wait for all
+// of them before every claim); the asm waits for its own result.
+__device__ __forceinline__ int lds_fetch_add(int* counter, int v) {
+  const uint32_t addr =
+      (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)counter);
+  int old;
+  asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(old) : "v"(addr), "v"(v) : "memory");
+  return old;
+}
+
 // The work-group's tiles pt0 + [0, count) are handed out to its waves from an
 // LDS counter, so waves that run ahead (the SIMDs favour older waves) take
 // more tiles and all finish close together. Which wave sums which tile then
 // depends on timing, so results can differ between runs in the last bits.
-// Each wave keeps two tiles in registers: on entry `ta` holds the loads of its
-// tile ia and `tb` those of ib (> ia); a buffer is refilled with the next
-// handed-out tile as soon as it has been consumed. That tile's index is
-// claimed before the consumed tile's arithmetic, so the counter's round trip
-// overlaps it.
-template <int D, int NT, bool Q8, typename Load>
-__device__ __forceinline__ void run_tiles(Tile<D>& ta, Tile<D>& tb, WaveState<D, NT>& st, const Load& load,
-                                          const QOperand<D, NT, Q8>& qop, float kscale,
+// Each wave stages two tiles in its LDS slots: on entry s0 receives its tile
+// ia and s1 its tile ib (> ia). A slot is read into the register tile, then
+// refilled with the next handed-out tile (claimed before the read, so the
+// counter's round trip overlaps it) before the arithmetic of the tile just
+// read, so two tiles are always on their way from memory.
+template <int D, int NT, bool Q8, typename Stage>
+__device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, WaveState<D, NT>& st,
+                                          const Stage& stage, const QOperand<D, NT, Q8>& qop, float kscale,
                                           int pt0, int count, int ia, int ib, int* next, int lane, int lo, int hi,
                                           int g, int new_tile, const float (&xk)[D / 64], const float (&xv)[D / 64],
                                           int8_t* row_lds, bool write, int8_t* krow, int8_t* vrow, float* ks,
                                           float* vs) {
+  constexpr int NDMA = Slot<D>::kDma;
   const int c = lane & 15;
   const auto claim = [&]() {
     int r = 0;
-    if (lane == 0) r = atomicAdd(next, 1);
+    if (lane == 0) r = lds_fetch_add(next, 1);
     return r;
+  };
+  // One tile from `slot`: wait for its loads (only the other slot's may still
+  // be in flight), read it, refill the slot, compute.
+  const auto step = [&](char* slot, int& i, int claimed) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA));
+    read_slot<D>(cur, slot, g, c);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the slot's reads (and the claim) are done
+    const int in = __builtin_amdgcn_readfirstlane(claimed);
+    if (i == new_tile) {
+      encode_new_row<D>(cur, xk, xv, row_lds, hi - 1 - (pt0 + i) * kTileKeys, g, c, lane, write, krow, vrow, ks,
+                        vs);
+      // the row's stores count with the staging loads: let them drain so the
+      // counts above keep meaning "the other slot's loads"
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    stage(slot, in);
+    compute_tile<D, NT, Q8>(cur, st, qop, kscale, (pt0 + i) * kTileKeys, lo, hi, g);
+    i = in;
   };
   // ia < ib at the top of the loop and handed-out indices only grow, so once
   // ia is past the end so is ib (and vice versa in the middle).
   while (ia < count) {
-    int na = claim();
-    if (ia == new_tile)
-      encode_new_row<D>(ta, xk, xv, row_lds, hi - 1 - (pt0 + ia) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
-    compute_tile<D, NT, Q8>(ta, st, qop, kscale, (pt0 + ia) * kTileKeys, lo, hi, g);
-    ia = __builtin_amdgcn_readfirstlane(na);
-    load(ta, ia);
+    step(s0, ia, claim());
     if (ib >= count) break;
-    int nb = claim();
-    if (ib == new_tile)
-      encode_new_row<D>(tb, xk, xv, row_lds, hi - 1 - (pt0 + ib) * kTileKeys, g, c, lane, write, krow, vrow, ks, vs);
-    compute_tile<D, NT, Q8>(tb, st, qop, kscale, (pt0 + ib) * kTileKeys, lo, hi, g);
-    ib = __builtin_amdgcn_readfirstlane(nb);
-    load(tb, ib);
+    step(s1, ib, claim());
   }
 }
 
@@ -522,8 +631,17 @@ void decode_partition_kernel(DecodeParams p) {
   constexpr int HP = NT * 16;  // padded head count
   constexpr int NK = NT * DPL; // accumulator tiles per lane
 
-  // Raw accumulators of the waves in register order: [wave][tile nt*DPL+mt][lane][r].
-  __shared__ __attribute__((aligned(16))) float sm_acc[WV * NK * kWave * 4];
+  // Each wave's two staging slots (separate arrays, so the compiler can tell
+  // a slot being read from the one being filled). After its last tile a wave
+  // parks its accumulators in its own slots: tile nt*DPL+mt of the state,
+  // 1 KB per tile in lane order, the first half of the tiles in slot 0.
+  __shared__ __attribute__((aligned(16))) char sm_s0[WV][Slot<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) char sm_s1[WV][Slot<D>::kBytes];
+  static_assert((NK / 2) * kWave * 16 <= Slot<D>::kBytes, "parked state fits the slots");
+  const auto parked = [&](int w, int t) -> float* {
+    char* base = t < NK / 2 ? sm_s0[w] : sm_s1[w];
+    return reinterpret_cast<float*>(base + (t % (NK / 2)) * (kWave * 16));
+  };
   __shared__ float sm_m[WV][HP];
   __shared__ float sm_l[WV][HP];
   __shared__ int sm_next;  // next tile (relative to pt0) to hand out
@@ -538,10 +656,8 @@ void decode_partition_kernel(DecodeParams p) {
   const int h0 = p.heads_per_group * (int)blockIdx.z;   // first head of this group
   const int Hg = min(Hq - h0, min(p.heads_per_group, NT * 16));    // heads of this group
 
-  TileOffsets off;
-  off.k = (uint32_t)(c * D + g * (D / 4));
-  off.v = (uint32_t)(4 * g * D + (D / 16) * c);
-  off.s = (uint32_t)(16 * g);
+  const uint32_t lane_kv = stage_lane_offset<D>(lane);
+  const uint32_t lane_sc = (uint32_t)(lane & 31) * 4;
 
   // One segment: sequence b, its visible tiles [seg_lo, seg_lo + seg_len)
   // (relative to the first visible tile; tiles past the visible range are
@@ -614,10 +730,11 @@ void decode_partition_kernel(DecodeParams p) {
   // A windowed layer needs the length to place its tiles. (Issuing the second
   // tile this early too measured slower: the first work-groups' loads then
   // delay the q loads of those dispatched last.)
-  Tile<D> ta, tb;
+  char* const s0 = sm_s0[wave];
+  char* const s1 = sm_s1[wave];
   if (!WINDOWED && !PAGED) {
     const int t0 = seg_lo + wave;
-    load_tile<D>(ta, sb, off, t0 * kTileKeys, wave < seg_len && (t0 + 1) * kTileKeys <= p.L_cap);
+    stage_tile<D>(s0, sb, lane_kv, lane_sc, t0 * kTileKeys, wave < seg_len && (t0 + 1) * kTileKeys <= p.L_cap);
   }
 
   int n = __builtin_amdgcn_readfirstlane(n_raw);  // same for the whole work-group
@@ -654,10 +771,10 @@ void decode_partition_kernel(DecodeParams p) {
     return ((int64_t)e << p.log2_bs) | (pos & ((1 << p.log2_bs) - 1));
   };
   const int64_t new_row = (new_tile >= 0 && new_tile < count) ? phys_row(n - 1) : 0;
-  // Loads of tile i of the partition (i >= count: nothing is read).
-  const auto load = [&](Tile<D>& t, int i) {
+  // Staging loads of tile i of the partition (i >= count: nothing is read).
+  const auto stage = [&](char* slot, int i) {
     if (!PAGED) {
-      load_tile<D>(t, sb, off, (pt0 + i) * kTileKeys, i < count);
+      stage_tile<D>(slot, sb, lane_kv, lane_sc, (pt0 + i) * kTileKeys, i < count);
     } else {
       SeqBuffers tsb;
       const int64_t row = i < count ? phys_row((pt0 + i) * kTileKeys) : 0;
@@ -666,11 +783,11 @@ void decode_partition_kernel(DecodeParams p) {
       tsb.v = make_rsrc(p.v + row * D, kvb);
       tsb.ks = make_rsrc(p.ks + row, scb);
       tsb.vs = make_rsrc(p.vs + row, scb);
-      load_tile<D>(t, tsb, off, 0, i < count);
+      stage_tile<D>(slot, tsb, lane_kv, lane_sc, 0, i < count);
     }
   };
-  if (WINDOWED || PAGED) load(ta, wave);
-  load(tb, wave + WV);
+  if (WINDOWED || PAGED) stage(s0, wave);
+  stage(s1, wave + WV);
 
   // Q^T as the B operand in fp16: the wave scales q by an exact power of two
   // that puts its largest |q| in [2^14, 2^15) and folds the scale into its
@@ -712,17 +829,21 @@ void decode_partition_kernel(DecodeParams p) {
   }
   st.vexp = -1000;
 
-  run_tiles<D, NT, Q8>(ta, tb, st, load, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g,
+  Tile<D> cur;
+  run_tiles<D, NT, Q8>(s0, s1, cur, st, stage, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g,
                    new_tile, xk, xv, sm_new[wave], blockIdx.z == 0, p.k_w + new_row * D, p.v_w + new_row * D,
                    p.ks_w + new_row, p.vs_w + new_row);
 
   // ---- combine the waves of the work-group -----------------------------------
   // Each wave parks its raw accumulators and (m, l) per head in LDS (lane-ordered
-  // 16-byte stores, conflict free); after one barrier, job (nt, g', c, r)
+  // 16-byte stores, conflict free) once its own staging loads have landed (the
+  // last ones, of tiles past the end, write zeros into its slots); after one
+  // barrier, job (nt, g', c, r)
   // combines all waves' values of head 16nt + c at dims DPL*(4g' + r) + 0..DPL-1,
   // which are contiguous in the output row.
   // Parked states are normalised, o / l with the value scale folded back
   // (2^vexp), so that no partial sum can overflow fp32.
+  __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float l = quad_sum(st.l_run[nt]);
@@ -736,7 +857,7 @@ void decode_partition_kernel(DecodeParams p) {
       f32x4 o = st.oacc[mt][nt] * inv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] = __builtin_ldexpf(o[r], st.vexp);
-      *reinterpret_cast<f32x4*>(&sm_acc[((wave * NK + nt * DPL + mt) * kWave + lane) * 4]) = o;
+      *reinterpret_cast<f32x4*>(parked(wave, nt * DPL + mt) + lane * 4) = o;
     }
   }
   __syncthreads();
@@ -768,7 +889,7 @@ void decode_partition_kernel(DecodeParams p) {
       float acc = 0.f;
 #pragma unroll
       for (int w = 0; w < WV; ++w)
-        acc += f[w] * sm_acc[((w * NK + nt * DPL + mt) * kWave + 16 * gq + cc) * 4 + rr];
+        acc += f[w] * parked(w, nt * DPL + mt)[(16 * gq + cc) * 4 + rr];
       o[mt] = acc * invL;  // normalised: the output itself, or this partition's share
     }
     if (h < Hg) {
