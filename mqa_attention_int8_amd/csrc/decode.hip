@@ -118,11 +118,10 @@ struct DecodeParams {
   int32_t num_blocks;
   float* ws_o;       // [slots, Hq, D] partition outputs, normalised (natural d order)
   float2* ws_ml;     // [slots, Hq] (offset m in log2 units, sum l of 2^(z - m))
-  // Balanced plan of a ragged batch (written by decode_plan_kernel): header
-  // {chunk c, total tiles T, pieces}, then per work-group the piece {sequence,
-  // first tile, tiles, whole sequence?}, then per sequence {first piece,
-  // pieces}.
+  // Balanced plan of a ragged batch, written by decode_plan_kernel (layout
+  // there); plan_G work-groups per head group.
   const int32_t* plan;
+  int32_t plan_G;
   int32_t B;
   int32_t L_cap;
   int32_t max_len;          // lengths are clamped to [0, max_len]: the host's max_seq_len (<= L_cap)
@@ -617,8 +616,8 @@ __device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, Wave
 // tiles then depend on the sequence length); otherwise to all of them.
 // PAGED: the cache is a block pool addressed through p.table.
 // Q8: int8 queries (p.q8, p.q_scale) and int8 MFMA for Q K^T.
-// RAGGED: balanced plan (one piece of a sequence per work-group, see
-// DecodeParams and decode_plan_kernel).
+// RAGGED: balanced plan (a range of the batch's tiles per work-group, one or
+// more sequence segments; see decode_plan_kernel).
 template <int D, int NT, bool WINDOWED, bool PAGED, bool Q8, bool RAGGED>
 __global__ __launch_bounds__(64 * kWavesPerWG) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partition_kernel(DecodeParams p) {
@@ -911,13 +910,18 @@ void decode_partition_kernel(DecodeParams p) {
     const int part = blockIdx.x, tpp = p.tiles_per_part;
     segment(blockIdx.y, part * tpp, tpp, (int64_t)blockIdx.y * p.num_parts + part, p.num_parts == 1);
   } else {
-    // one piece of the balanced plan per work-group; work-groups past the
-    // last piece have nothing to do
-    const int4 piece = *reinterpret_cast<const int4*>(p.plan + 4 + 4 * blockIdx.x);
-    const int b = __builtin_amdgcn_readfirstlane(piece.x);
-    if (b >= p.B) return;
-    segment(b, __builtin_amdgcn_readfirstlane(piece.y), __builtin_amdgcn_readfirstlane(piece.z),
-            (int64_t)blockIdx.x, piece.w != 0);
+    // the segments of this work-group's range of the balanced plan, in order
+    // (each segment begins with a barrier, so the previous one's combine is
+    // over before its LDS is reused)
+    const int2 wg = *reinterpret_cast<const int2*>(p.plan + 4 + 2 * blockIdx.x);
+    const int first = __builtin_amdgcn_readfirstlane(wg.x);
+    const int nseg = __builtin_amdgcn_readfirstlane(wg.y);
+    const int32_t* segs = p.plan + 4 + 2 * p.plan_G;
+    for (int k = 0; k < nseg; ++k) {
+      const int4 sg = *reinterpret_cast<const int4*>(segs + 4 * (first + k));
+      segment(__builtin_amdgcn_readfirstlane(sg.x), __builtin_amdgcn_readfirstlane(sg.y),
+              __builtin_amdgcn_readfirstlane(sg.z), (int64_t)(first + k), __builtin_amdgcn_readfirstlane(sg.w) != 0);
+    }
   }
 }
 
@@ -935,7 +939,8 @@ template <int D>
 __global__ __launch_bounds__(256 * kMergeMaxSlices) void decode_merge_kernel(const float* __restrict__ ws_o,
                                                                              const float2* __restrict__ ws_ml,
                                                                              float* __restrict__ out, int Hq, int P,
-                                                                             const int32_t* __restrict__ plan, int G) {
+                                                                             const int32_t* __restrict__ plan,
+                                                                             int seq_off) {
   constexpr int D4 = D / 4;
   constexpr int HPB = 256 / D4;  // heads per block
   __shared__ f32x4 s_acc[kMergeMaxSlices - 1][256];
@@ -948,11 +953,11 @@ __global__ __launch_bounds__(256 * kMergeMaxSlices) void decode_merge_kernel(con
   const int d0 = 4 * (t % D4);
   const bool live_h = h < Hq;
   // States of sequence b: slots s0 .. s0 + P - 1. Balanced plan: the
-  // sequence's pieces wrote consecutive slots; a sequence in one piece was
+  // sequence's segments wrote consecutive slots; a sequence in one segment was
   // written to the output directly, one with no visible key gets zeros.
   int64_t s0 = (int64_t)b * P;
   if (plan != nullptr) {
-    const int2 sq = *reinterpret_cast<const int2*>(plan + 4 + 4 * G + 2 * b);
+    const int2 sq = *reinterpret_cast<const int2*>(plan + seq_off + 2 * b);
     if (sq.y == 1) return;
     s0 = sq.x;
     P = sq.y;
@@ -1010,15 +1015,20 @@ __global__ __launch_bounds__(256 * kMergeMaxSlices) void decode_merge_kernel(con
 
 // ---------------------------------------------------------------------------
 // Balanced plan of a ragged batch (one work-group of kPlanThreads threads).
-// With T the visible 32-key tiles of all sequences and G the work-groups
-// that fill the chip once, c = max(8, ceil(T / G)); sequence b (t_b visible
-// tiles) is cut into n_b = ceil(t_b / c) pieces of near-equal size, so no
-// piece exceeds c tiles whatever the lengths, and there are at most G + B
-// pieces, one work-group each, in sequence order (the pieces of a sequence
-// use consecutive partial-state slots). Written: header {c, T, pieces, 0};
-// per work-group of the launch (NW of them) its piece {b, first tile, tiles,
-// n_b == 1}, or b = B when it has none; per sequence {first piece, n_b}.
-// Lengths are clamped exactly as the attention kernel clamps them.
+// The visible 32-key tiles of all sequences, in sequence order, form one
+// list of T tiles; with G the work-groups that fill the chip once, chunk
+// c = max(8, ceil(T / G)) and work-group j takes tiles [j c, (j + 1) c) of
+// the list, so exactly ceil(T / c) <= G work-groups have work and none has
+// more than c tiles, whatever the lengths. The part of sequence b that falls
+// in work-group j's range is a segment; a work-group's segments are
+// consecutive in (sequence, work-group) order, which is also the order of the
+// partial-state slots: sequence b (P_b tiles before it, t_b of its own)
+// spans work-groups P_b / c .. (P_b + t_b - 1) / c and owns that many
+// consecutive slots. Written (int32 words): header {c, T, segments,
+// work-groups with work}; per work-group (G) {first segment, segments};
+// per segment (at most G + B) {b, first tile, tiles, whole sequence?}; per
+// sequence (B) {first segment, segments}. Lengths are clamped exactly as the
+// attention kernel clamps them.
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 constexpr int kMinChunk = kWavesPerWG;  // at least one tile per wave
@@ -1059,48 +1069,66 @@ __device__ __forceinline__ int block_inclusive_sum(int v, int* sm, int& total) {
 
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t* __restrict__ seq_lens,
                                                                    int32_t* __restrict__ plan, int B, int window,
-                                                                   int max_len, int G, int NW) {
+                                                                   int max_len, int G) {
   __shared__ int sm[kPlanThreads / 64];
   const int tid = threadIdx.x;
   int part = 0;
   for (int b = tid; b < B; b += kPlanThreads) part += visible_tiles(seq_lens[b], window, max_len);
   int total;
   (void)block_inclusive_sum(part, sm, total);
-  const int chunk = max(kMinChunk, (total + G - 1) / G);
-  int32_t* pieces = plan + 4;
-  int32_t* seqs = plan + 4 + 4 * NW;
-  int carry = 0;
+  const int chunk = (int)max<int64_t>(kMinChunk, ((int64_t)total + G - 1) / G);
+  const int busy = (int)(((int64_t)total + chunk - 1) / chunk);
+  int32_t* wg = plan + 4;
+  int32_t* segs = plan + 4 + 2 * G;
+  int32_t* seqs = segs + 4 * (G + B);
+  int carry_t = 0, carry_s = 0;
   for (int base = 0; base < B; base += kPlanThreads) {
     const int b = base + tid;
     const int t = b < B ? visible_tiles(seq_lens[b], window, max_len) : 0;
-    const int n = (t + chunk - 1) / chunk;
-    int tot;
-    const int first = carry + block_inclusive_sum(n, sm, tot) - n;
+    int tot_t, tot_s;
+    const int P = carry_t + block_inclusive_sum(t, sm, tot_t) - t;   // tiles before sequence b
+    const int j1 = P / chunk, j2 = (int)(((int64_t)P + t - 1) / chunk);
+    const int n = t > 0 ? j2 - j1 + 1 : 0;
+    const int S = carry_s + block_inclusive_sum(n, sm, tot_s) - n;  // segments before sequence b
     if (b < B) {
-      *reinterpret_cast<int2*>(seqs + 2 * b) = make_int2(first, n);
+      *reinterpret_cast<int2*>(seqs + 2 * b) = make_int2(S, n);
       for (int k = 0; k < n; ++k) {
-        const int lo = (int)((int64_t)k * t / n), hi = (int)((int64_t)(k + 1) * t / n);
-        *reinterpret_cast<int4*>(pieces + 4 * (first + k)) = make_int4(b, lo, hi - lo, n == 1);
+        const int j = j1 + k;
+        const int64_t start = (int64_t)j * chunk;  // 64-bit: (j + 1) c may pass 2^31
+        const int lo = (int)max(start, (int64_t)P), hi = (int)min(start + chunk, (int64_t)P + t);
+        *reinterpret_cast<int4*>(segs + 4 * (S + k)) = make_int4(b, lo - P, hi - lo, n == 1);
+        if (lo == start) wg[2 * j] = S + k;  // the segment that starts work-group j's range
       }
     }
-    carry += tot;
+    carry_t += tot_t;
+    carry_s += tot_s;
   }
-  for (int w = carry + tid; w < NW; w += kPlanThreads)
-    *reinterpret_cast<int4*>(pieces + 4 * w) = make_int4(B, 0, 0, 0);
+  __syncthreads();  // every busy work-group's first segment is written
+  for (int j = tid; j < G; j += kPlanThreads) {
+    if (j < busy) {
+      const int next = j + 1 < busy ? wg[2 * (j + 1)] : carry_s;
+      wg[2 * j + 1] = next - wg[2 * j];
+    } else {
+      *reinterpret_cast<int2*>(wg + 2 * j) = make_int2(0, 0);
+    }
+  }
   if (tid == 0) {
     plan[0] = chunk;
     plan[1] = total;
-    plan[2] = carry;
-    plan[3] = 0;
+    plan[2] = carry_s;
+    plan[3] = busy;
   }
 }
+
+// Words of the balanced plan's area (layout above decode_plan_kernel).
+constexpr size_t ragged_plan_words(size_t G, size_t B) { return 4 + 2 * G + 4 * (G + B) + 2 * B; }
 
 template <int D, int NT, bool PAGED, bool Q8, bool RAGGED>
 void launch_partitions(const DecodeParams& prm, int B, int G, hipStream_t stream) {
   const dim3 block(64 * kWavesPerWG);
   const int groups = (prm.Hq + prm.heads_per_group - 1) / prm.heads_per_group;
-  // balanced plan: one work-group per piece, at most G + B pieces
-  const dim3 grid = RAGGED ? dim3(G + B, 1, groups) : dim3(prm.num_parts, B, groups);
+  // balanced plan: G work-groups per head group, each over its range of the plan
+  const dim3 grid = RAGGED ? dim3(G, 1, groups) : dim3(prm.num_parts, B, groups);
   if (prm.window > 0)
     hipLaunchKernelGGL((decode_partition_kernel<D, NT, true, PAGED, Q8, RAGGED>), grid, block, 0, stream, prm);
   else
@@ -1180,7 +1208,7 @@ DecodePlan plan_decode_ragged(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_
   pl.heads_per_group = kHeadsPerGroup;
   pl.tiles_per_part = 0;
   pl.num_parts = 0;
-  const size_t plan_words = 4 + 4 * ((size_t)G + (size_t)B) + 2 * (size_t)B;
+  const size_t plan_words = ragged_plan_words((size_t)G, (size_t)B);
   const size_t slots = ((size_t)G + (size_t)B) * (size_t)Hq;
   pl.ws_bytes = align_up(plan_words * sizeof(int32_t), 256) + align_up(slots * sizeof(float2), 256) +
                 align_up(slots * (size_t)D * sizeof(float), 256);
@@ -1255,11 +1283,12 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layo
   prm.ws_o = nullptr;
   prm.ws_ml = nullptr;
   prm.plan = nullptr;
+  prm.plan_G = 0;
   prm.B = B;
   const int G = plan.ragged_groups;
   if (G > 0) {
     // balanced plan: plan area, then the states of G + B slots
-    const size_t plan_words = 4 + 4 * ((size_t)G + (size_t)B) + 2 * (size_t)B;
+    const size_t plan_words = ragged_plan_words((size_t)G, (size_t)B);
     const size_t slots = ((size_t)G + (size_t)B) * (size_t)Hq;
     char* ws = static_cast<char*>(workspace);
     int32_t* plan_area = reinterpret_cast<int32_t*>(ws);
@@ -1268,8 +1297,9 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layo
     ws += align_up(slots * sizeof(float2), 256);
     prm.ws_o = reinterpret_cast<float*>(ws);
     prm.plan = plan_area;
+    prm.plan_G = G;
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, plan_area, B, window,
-                       prm.max_len, G, G + B);
+                       prm.max_len, G);
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
   } else if (plan.num_parts > 1) {
     const size_t slots = (size_t)B * (size_t)plan.num_parts * (size_t)Hq;
@@ -1290,10 +1320,10 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layo
     const dim3 block(256 * slices);
     if (D == 128)
       hipLaunchKernelGGL(decode_merge_kernel<128>, grid, block, 0, stream, prm.ws_o, prm.ws_ml, out, Hq,
-                         plan.num_parts, prm.plan, G + B);
+                         plan.num_parts, prm.plan, (int)(ragged_plan_words((size_t)G, (size_t)B) - 2 * (size_t)B));
     else
       hipLaunchKernelGGL(decode_merge_kernel<64>, grid, block, 0, stream, prm.ws_o, prm.ws_ml, out, Hq,
-                         plan.num_parts, prm.plan, G + B);
+                         plan.num_parts, prm.plan, (int)(ragged_plan_words((size_t)G, (size_t)B) - 2 * (size_t)B));
     if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
   }
   return MQA_OK;
