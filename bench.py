@@ -676,9 +676,9 @@ def cpu_baseline(budget_s: float):
     Per sequence, the timed work is what one block step does: encode the new
     token's K and V rows into the three buffers' owners, then the six layers
     (the global one over the sequence's whole context, the five window layers
-    over its last 1024 keys). Sequences' caches are generated and encoded
-    outside the timed region; sequences are taken in order until about
-    ``budget_s`` seconds of timed work."""
+    over its last 1024 keys). Every sequence's cache is generated and encoded
+    once, outside the timed region; then passes over the batch are timed,
+    sequence by sequence, until about ``budget_s`` seconds of timed work."""
     import numpy as np
     from threadpoolctl import threadpool_info
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
@@ -688,7 +688,7 @@ def cpu_baseline(budget_s: float):
     Hq, D = w.Hq, w.D
     lens = w.lens()
     t_all = time.perf_counter()
-    done, t_work, keys = 0, 0.0, 0
+    cases = []
     for b in range(w.B):
         n = int(lens[b])
         g = synth.rng(3, synth.T_K, 5000 + b)
@@ -702,28 +702,32 @@ def cpu_baseline(budget_s: float):
             bufs[name] = (kq, ks, vq, vs)
         qs = [synth.q_bf16(g, (1, Hq, D)) for _ in w.layers]
         knew, vnew = synth.normal_f32(g, (1, D)), synth.normal_f32(g, (1, D))
-        t0 = time.perf_counter()
-        for name in ("G", "A", "Bf"):             # the owners' fused append: the new token is the last row
-            kq, ks, vq, vs = bufs[name]
-            kq[0, -1], ks[0, -1] = oracle.quantize_rows(knew[0])
-            vq[0, -1], vs[0, -1] = oracle.quantize_rows(vnew[0])
-        for li, (name, win) in enumerate(w.layers):
-            kq, ks, vq, vs = bufs[name]
-            rows = kq.shape[1]
-            oracle.decode_ref(qs[li], kq, ks, vq, vs, np.array([rows], np.int32), win)
-        t_work += time.perf_counter() - t0
-        done += 1
-        keys += n + 5 * min(n, 1024)
-        if t_work >= budget_s:
-            break
+        cases.append((n, bufs, qs, knew, vnew))
+    done, t_work, keys = 0, 0.0, 0
+    while t_work < budget_s:
+        for n, bufs, qs, knew, vnew in cases:
+            t0 = time.perf_counter()
+            for name in ("G", "A", "Bf"):             # the owners' fused append: the new token is the last row
+                kq, ks, vq, vs = bufs[name]
+                kq[0, -1], ks[0, -1] = oracle.quantize_rows(knew[0])
+                vq[0, -1], vs[0, -1] = oracle.quantize_rows(vnew[0])
+            for li, (name, win) in enumerate(w.layers):
+                kq, ks, vq, vs = bufs[name]
+                rows = kq.shape[1]
+                oracle.decode_ref(qs[li], kq, ks, vq, vs, np.array([rows], np.int32), win)
+            t_work += time.perf_counter() - t0
+            done += 1
+            keys += n + 5 * min(n, 1024)
+            if t_work >= budget_s:
+                break
     info = threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     blas = [{"api": i.get("internal_api"), "version": i.get("version"), "threads": i.get("num_threads")}
             for i in info]
     return {"value": done / t_work, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of the {w.B} sequences of one hybrid block step (append + 1 global layer over "
-                      f"the whole context + 5 window-1024 layers; {keys} visible keys), numpy float64 oracle, "
-                      f"{t_work:.1f} s of timed work",
+            "sample": f"{done} sequence-steps over the {w.B} sequences of the hybrid block (each: append + 1 "
+                      f"global layer over the whole context + 5 window-1024 layers; {keys} visible keys in all), "
+                      f"numpy float64 oracle, {t_work:.1f} s of timed work",
             "cpu_model": host_description(), "host_cpus": len(os.sched_getaffinity(0)),
             "numpy": np.__version__, "blas": blas, "wall_s": time.perf_counter() - t_all}
 
