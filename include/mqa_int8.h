@@ -447,6 +447,21 @@ int mqa_kv_blocks_to_device(const mqa_kv_cache* bufs, int32_t n_bufs, int32_t B,
                             const int64_t* slots, const void* host_pool, int64_t pool_slots,
                             void* stream);
 
+/* mqa_set_deterministic - choose how decode kernels hand tiles to waves.
+ * [workshop transcript 00:48:59-00:49:13: the online softmax is an exact
+ * rewrite of the softmax, so only the order of the floating-point sums can
+ * differ between two runs.] By default (0) the 32-key tiles of a work-group
+ * go to whichever wave asks first, which balances the waves but lets the
+ * order of the per-wave sums depend on timing: two runs on the same inputs
+ * may differ in the last bits. With enable != 0, wave w of a work-group takes
+ * the fixed tiles w, w + 8, w + 16, ..., and every decode entry point
+ * (mqa_decode*, including the append, ragged, paged, int8-query and
+ * allocation-free ones) returns bitwise identical results for identical
+ * inputs, plan and device. Process-wide; read when a call is launched (a
+ * captured graph keeps the setting it was captured with). Returns the
+ * previous setting. Never fails. */
+int mqa_set_deterministic(int enable);
+
 /* Static description of a status code (never NULL). */
 const char* mqa_status_string(int status);
 

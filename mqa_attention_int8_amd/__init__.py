@@ -11,4 +11,4 @@ from .binding import (KVView, MQAError, append_kv, kv_quantize_int8, load_librar
                       mqa_decode_paged_workspace_bytes, mqa_prefill_chunk_paged, mqa_decode_q8,
                       mqa_decode_append_q8, mqa_decode_ragged, mqa_decode_append_ragged,
                       mqa_decode_ragged_workspace_bytes, ragged_workspace, PrefixCache, host_pool, kv_block_bytes,
-                      mqa_kv_blocks_to_host, mqa_kv_blocks_to_device)
+                      mqa_kv_blocks_to_host, mqa_kv_blocks_to_device, mqa_set_deterministic)

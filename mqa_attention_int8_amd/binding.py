@@ -129,12 +129,20 @@ def load_library() -> ctypes.CDLL:
         lib.mqa_kv_blocks_to_device.argtypes = [ctypes.POINTER(mqa_kv_cache), i32, i32, i32, i64, i64, i32, i32, vp,
                                                 vp, i64, vp]
         lib.mqa_kv_blocks_to_device.restype = ctypes.c_int
+        lib.mqa_set_deterministic.argtypes = [ctypes.c_int]
+        lib.mqa_set_deterministic.restype = ctypes.c_int
         _lib = lib
         return lib
 
 
 def mqa_status_string(code: int) -> str:
     return load_library().mqa_status_string(int(code)).decode()
+
+
+def mqa_set_deterministic(enable: bool) -> bool:
+    """Fixed tile-to-wave assignment in decode calls launched from now on
+    (bitwise repeatable results); returns the previous setting."""
+    return bool(load_library().mqa_set_deterministic(1 if enable else 0))
 
 
 def _check(code: int, where: str):

@@ -99,6 +99,8 @@ int check_decode_common(const uint16_t* q, const int32_t* seq_lens, const float*
 
 extern "C" {
 
+int mqa_set_deterministic(int enable) { return mqa::set_deterministic(enable != 0) ? 1 : 0; }
+
 const char* mqa_status_string(int status) {
   switch (status) {
     case MQA_OK: return "ok";

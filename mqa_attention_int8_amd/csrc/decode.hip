@@ -122,6 +122,7 @@ struct DecodeParams {
   // there); plan_G work-groups per head group.
   const int32_t* plan;
   int32_t plan_G;
+  int32_t fixed_tiles;      // != 0: wave w takes tiles w, w + 8, ... (bitwise repeatable)
   int32_t B;
   int32_t L_cap;
   int32_t max_len;          // lengths are clamped to [0, max_len]: the host's max_seq_len (<= L_cap)
@@ -565,7 +566,9 @@ __device__ __forceinline__ int lds_fetch_add(int* counter, int v) {
 // The work-group's tiles pt0 + [0, count) are handed out to its waves from an
 // LDS counter, so waves that run ahead (the SIMDs favour older waves) take
 // more tiles and all finish close together. Which wave sums which tile then
-// depends on timing, so results can differ between runs in the last bits.
+// depends on timing, so results can differ between runs in the last bits;
+// with `fixed` (the deterministic setting) wave w takes tiles w, w + 8, ...
+// instead, and every sum has a fixed order.
 // Each wave stages two tiles in its LDS slots: on entry s0 receives its tile
 // ia and s1 its tile ib (> ia). A slot is read into the register tile, then
 // refilled with the next handed-out tile (claimed before the read, so the
@@ -577,10 +580,13 @@ __device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, Wave
                                           int pt0, int count, int ia, int ib, int* next, int lane, int lo, int hi,
                                           int g, int new_tile, const float (&xk)[D / 64], const float (&xv)[D / 64],
                                           int8_t* row_lds, bool write, int8_t* krow, int8_t* vrow, float* ks,
-                                          float* vs) {
+                                          float* vs, bool fixed) {
   constexpr int NDMA = Slot<D>::kDma;
   const int c = lane & 15;
-  const auto claim = [&]() {
+  // the next tile for the slot that holds tile i: the counter's, or with a
+  // fixed assignment the slot's next one (the wave's two slots alternate)
+  const auto claim = [&](int i) {
+    if (fixed) return i + 2 * kWavesPerWG;
     int r = 0;
     if (lane == 0) r = lds_fetch_add(next, 1);
     return r;
@@ -606,9 +612,9 @@ __device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, Wave
   // ia < ib at the top of the loop and handed-out indices only grow, so once
   // ia is past the end so is ib (and vice versa in the middle).
   while (ia < count) {
-    step(s0, ia, claim());
+    step(s0, ia, claim(ia));
     if (ib >= count) break;
-    step(s1, ib, claim());
+    step(s1, ib, claim(ib));
   }
 }
 
@@ -831,7 +837,7 @@ void decode_partition_kernel(DecodeParams p) {
   Tile<D> cur;
   run_tiles<D, NT, Q8>(s0, s1, cur, st, stage, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g,
                    new_tile, xk, xv, sm_new[wave], blockIdx.z == 0, p.k_w + new_row * D, p.v_w + new_row * D,
-                   p.ks_w + new_row, p.vs_w + new_row);
+                   p.ks_w + new_row, p.vs_w + new_row, p.fixed_tiles != 0);
 
   // ---- combine the waves of the work-group -----------------------------------
   // Each wave parks its raw accumulators and (m, l) per head in LDS (lane-ordered
@@ -1248,6 +1254,12 @@ void* static_scratch() {
   return ptr;
 }
 
+namespace {
+std::atomic<bool> g_fixed_tiles{false};
+}  // namespace
+
+bool set_deterministic(bool on) { return g_fixed_tiles.exchange(on); }
+
 int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layout, const int32_t* seq_lens,
                   int32_t B, int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,
                   void* workspace, const DecodePlan& plan, hipStream_t stream, const AppendRows* append,
@@ -1284,6 +1296,7 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layo
   prm.ws_ml = nullptr;
   prm.plan = nullptr;
   prm.plan_G = 0;
+  prm.fixed_tiles = g_fixed_tiles.load(std::memory_order_relaxed) ? 1 : 0;
   prm.B = B;
   const int G = plan.ragged_groups;
   if (G > 0) {

@@ -72,6 +72,10 @@ struct QueryInt8 {
 constexpr size_t kStaticScratchBytes = MQA_NOALLOC_SCRATCH_BYTES;
 void* static_scratch();
 
+// Fixed tile-to-wave assignment for decode launches (bitwise repeatable
+// results); returns the previous setting.
+bool set_deterministic(bool on);
+
 // q == nullptr with q8 set: the int8-query variant.
 int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layout, const int32_t* seq_lens,
                   int32_t B, int32_t Hq, int32_t D, int32_t window, float softmax_scale, float* out,

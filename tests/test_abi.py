@@ -342,3 +342,17 @@ def test_decode_plan_short_ranges(lib):
     assert m.mqa_decode_workspace_bytes(64, 32, 128, 4096, 2048) > 0      # 65 tiles: partitions
     assert m.mqa_decode_workspace_bytes(8, 32, 128, 1000, 0) == 0         # 32 tiles, 16 groups
     assert m.mqa_decode_workspace_bytes(200, 32, 128, 32768, 1024) > 0    # 400 groups > 256 units
+
+
+def test_deterministic_switch_returns_previous_setting(lib):
+    """mqa_set_deterministic is host-only: no device needed."""
+    lib.mqa_set_deterministic.argtypes = [ctypes.c_int]
+    lib.mqa_set_deterministic.restype = ctypes.c_int
+    first = lib.mqa_set_deterministic(1)
+    try:
+        assert first in (0, 1)
+        assert lib.mqa_set_deterministic(7) == 1      # any non-zero value turns it on
+        assert lib.mqa_set_deterministic(0) == 1
+        assert lib.mqa_set_deterministic(0) == 0
+    finally:
+        lib.mqa_set_deterministic(first)
