@@ -732,6 +732,11 @@ def cpu_baseline(budget_s: float):
             "numpy": np.__version__, "blas": blas, "wall_s": time.perf_counter() - t_all}
 
 
+# `--only` value of each entry of `extra` whose key differs from its name
+ONLY_KEY = {"decode_step_B64_L4096": "decode", "long_context": "long"}
+EXTRA_NAMES = ("decode_step_B64_L4096", "long_context", "prefill", "paged", "q8", "prefix_cache", "ceilings")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -759,15 +764,16 @@ def main():
     hyb = bench_hybrid(torch, m, acct, args, stream) if args.only in (None, "hybrid") else None
     extra = {}
     if not args.no_extra:
-        for name, fn in (("decode_step_B64_L4096", lambda: bench_decode(torch, m, acct, stream)),
-                         ("long_context", lambda: bench_long(torch, m, acct, stream)),
-                         ("prefill", lambda: bench_prefill(torch, m, acct, stream)),
-                         ("paged", lambda: bench_paged(torch, m, acct, stream)),
-                         ("q8", lambda: bench_q8(torch, m, acct, stream)),
-                         ("prefix_cache", lambda: bench_prefix_cache(torch, m, stream)),
-                         ("ceilings", lambda: bench_ceilings(torch, stream))):
-            key = {"decode_step_B64_L4096": "decode"}.get(name, name)
-            if args.only in (None, key):
+        fns = {"decode_step_B64_L4096": lambda: bench_decode(torch, m, acct, stream),
+               "long_context": lambda: bench_long(torch, m, acct, stream),
+               "prefill": lambda: bench_prefill(torch, m, acct, stream),
+               "paged": lambda: bench_paged(torch, m, acct, stream),
+               "q8": lambda: bench_q8(torch, m, acct, stream),
+               "prefix_cache": lambda: bench_prefix_cache(torch, m, stream),
+               "ceilings": lambda: bench_ceilings(torch, stream)}
+        for name in EXTRA_NAMES:
+            fn = fns[name]
+            if args.only in (None, ONLY_KEY.get(name, name)):
                 extra[name] = fn()
                 print(f"bench: {name} done", file=sys.stderr, flush=True)
     if hyb is None:

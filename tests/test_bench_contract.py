@@ -41,3 +41,20 @@ def test_counted_traffic_follows_the_sources(tmp_path, monkeypatch):
     (fake / "profiles" / name).write_text(json.dumps(rec))
     monkeypatch.setattr(bench.os.path, "abspath", lambda p: str(fake / "bench.py"))
     assert bench.counted_traffic(name) is None
+
+
+def test_every_only_choice_selects_a_workload():
+    """Each `--only` value names the headline, its global layer or one extra."""
+    import bench
+    ap_choices = None
+    for a in bench.build_parser()._actions if hasattr(bench, "build_parser") else []:
+        if a.dest == "only":
+            ap_choices = a.choices
+    if ap_choices is None:
+        import re
+        src = open(bench.__file__).read()
+        ap_choices = re.findall(r'"([a-z_0-9]+)"', src[src.index('"--only", choices=['):src.index('default=None, help="time a single')])
+    extras = {bench.ONLY_KEY.get(n, n) for n in bench.EXTRA_NAMES}
+    for c in ap_choices:
+        assert c in extras or c in ("hybrid", "hybrid_global"), c
+    assert extras <= set(ap_choices)
