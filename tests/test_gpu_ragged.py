@@ -1,7 +1,8 @@
-"""mqa_decode_ragged / mqa_decode_append_ragged (a planning kernel splits the
-visible tiles of all sequences into pieces of at most ceil(T / G) tiles, one
-work-group each) against the oracle, and against mqa_decode on the same
-inputs (the same arithmetic summed in another order)."""
+"""mqa_decode_ragged / mqa_decode_append_ragged (a planning kernel cuts the
+list of all sequences' visible tiles into ranges of at most max(8, ceil(T / G))
+tiles, one per work-group, which walks the sequence segments inside its
+range) against the oracle, and against mqa_decode on the same inputs (the
+same arithmetic summed in another order)."""
 import numpy as np
 import pytest
 import torch
@@ -53,6 +54,14 @@ def test_many_short_sequences():
     """1000 sequences of 0..300 keys: most are a single piece written directly."""
     lens = synth.ragged_lens(synth.rng(98, synth.T_LENS), 1000, 0, 300)
     ragged_case(98, 1000, 320, 8, 64, lens, 0, "1000 short")
+
+
+def test_planner_carries_over_several_passes():
+    """2500 sequences: the one-work-group planner walks the batch in three
+    passes of 1024 (prefix sums carried across passes), and every
+    work-group's range holds a dozen or more sequence segments."""
+    lens = synth.ragged_lens(synth.rng(103, synth.T_LENS), 2500, 0, 700)
+    ragged_case(103, 2500, 704, 8, 64, lens, 0, "2500 sequences")
 
 
 @pytest.mark.parametrize("Hq,D", [(64, 128), (8, 64), (20, 128)])
