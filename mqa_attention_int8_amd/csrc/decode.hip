@@ -220,9 +220,14 @@ __device__ __forceinline__ void stage_tile(char* slot, const SeqBuffers& sb, uin
 // of either slot it would wait for all of them (the caller waits for the
 // slot's own loads). Lane (g, c) reads K rows c and 16 + c (chunks
 // g*KV4 + w, swizzled by the row), V rows 16(i/4) + 4g + i%4 at byte
-// c*D/16, and the scales of keys 16hf + 4g .. +3.
+// c*D/16, and the scales of keys 16hf + 4g .. +3. The same block adds 1 to
+// the LDS word at each lane's `claim_addr` and returns its old value in
+// `claimed` (the work-group's tile counter for lane 0, a lane-private
+// dummy word for the others), so the claim of the wave's next tile shares
+// the reads' single wait.
 template <int D>
-__device__ __forceinline__ void read_slot(Tile<D>& t, const char* slot, int g, int c) {
+__device__ __forceinline__ void read_slot(Tile<D>& t, const char* slot, int g, int c, uint32_t claim_addr,
+                                          int& claimed) {
   constexpr int CH = Slot<D>::kCh;
   constexpr int HALF = 16 * D;  // bytes of 16 rows: rows r and r + 16 share the swizzle
   const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)slot);
@@ -237,30 +242,35 @@ __device__ __forceinline__ void read_slot(Tile<D>& t, const char* slot, int g, i
   }
   const uint32_t as = base + Slot<D>::kOffKs + 16 * g;
   static_assert(Slot<D>::kOffVs - Slot<D>::kOffKs == 256, "scale layout");
+  const uint32_t one = 1;
   if constexpr (D == 128) {
     u32x2 v[8];
     asm volatile(
-        "ds_read_b128 %0, %16\n\t"
-        "ds_read_b128 %1, %16 offset:2048\n\t"
-        "ds_read_b128 %2, %17\n\t"
-        "ds_read_b128 %3, %17 offset:2048\n\t"
-        "ds_read_b64 %4, %18\n\t"
-        "ds_read_b64 %5, %19\n\t"
-        "ds_read_b64 %6, %20\n\t"
-        "ds_read_b64 %7, %21\n\t"
-        "ds_read_b64 %8, %18 offset:2048\n\t"
-        "ds_read_b64 %9, %19 offset:2048\n\t"
-        "ds_read_b64 %10, %20 offset:2048\n\t"
-        "ds_read_b64 %11, %21 offset:2048\n\t"
-        "ds_read_b128 %12, %22\n\t"
-        "ds_read_b128 %13, %22 offset:64\n\t"
-        "ds_read_b128 %14, %22 offset:256\n\t"
-        "ds_read_b128 %15, %22 offset:320\n\t"
+        "ds_add_rtn_u32 %[cl], %[ca], %[one]\n\t"
+        "ds_read_b128 %[k00], %[ak0]\n\t"
+        "ds_read_b128 %[k10], %[ak0] offset:2048\n\t"
+        "ds_read_b128 %[k01], %[ak1]\n\t"
+        "ds_read_b128 %[k11], %[ak1] offset:2048\n\t"
+        "ds_read_b64 %[v0], %[av0]\n\t"
+        "ds_read_b64 %[v1], %[av1]\n\t"
+        "ds_read_b64 %[v2], %[av2]\n\t"
+        "ds_read_b64 %[v3], %[av3]\n\t"
+        "ds_read_b64 %[v4], %[av0] offset:2048\n\t"
+        "ds_read_b64 %[v5], %[av1] offset:2048\n\t"
+        "ds_read_b64 %[v6], %[av2] offset:2048\n\t"
+        "ds_read_b64 %[v7], %[av3] offset:2048\n\t"
+        "ds_read_b128 %[ks0], %[as]\n\t"
+        "ds_read_b128 %[ks1], %[as] offset:64\n\t"
+        "ds_read_b128 %[vs0], %[as] offset:256\n\t"
+        "ds_read_b128 %[vs1], %[as] offset:320\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(t.k[0][0]), "=&v"(t.k[1][0]), "=&v"(t.k[0][1]), "=&v"(t.k[1][1]), "=&v"(v[0]), "=&v"(v[1]),
-          "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(t.ks[0]),
-          "=&v"(t.ks[1]), "=&v"(t.vs[0]), "=&v"(t.vs[1])
-        : "v"(ak[0]), "v"(ak[1]), "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]), "v"(as));
+        : [k00] "=&v"(t.k[0][0]), [k10] "=&v"(t.k[1][0]), [k01] "=&v"(t.k[0][1]), [k11] "=&v"(t.k[1][1]),
+          [v0] "=&v"(v[0]), [v1] "=&v"(v[1]), [v2] "=&v"(v[2]), [v3] "=&v"(v[3]), [v4] "=&v"(v[4]),
+          [v5] "=&v"(v[5]), [v6] "=&v"(v[6]), [v7] "=&v"(v[7]), [ks0] "=&v"(t.ks[0]), [ks1] "=&v"(t.ks[1]),
+          [vs0] "=&v"(t.vs[0]), [vs1] "=&v"(t.vs[1]), [cl] "=&v"(claimed)
+        : [ak0] "v"(ak[0]), [ak1] "v"(ak[1]), [av0] "v"(av[0]), [av1] "v"(av[1]), [av2] "v"(av[2]),
+          [av3] "v"(av[3]), [as] "v"(as), [ca] "v"(claim_addr), [one] "v"(one)
+        : "memory");
     static_assert(HALF == 2048, "offsets above assume D = 128");
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -271,24 +281,29 @@ __device__ __forceinline__ void read_slot(Tile<D>& t, const char* slot, int g, i
     static_assert(D == 64 && HALF == 1024, "offsets below assume D = 64");
     uint32_t v[8];
     asm volatile(
-        "ds_read_b128 %0, %14\n\t"
-        "ds_read_b128 %1, %14 offset:1024\n\t"
-        "ds_read_b32 %2, %15\n\t"
-        "ds_read_b32 %3, %16\n\t"
-        "ds_read_b32 %4, %17\n\t"
-        "ds_read_b32 %5, %18\n\t"
-        "ds_read_b32 %6, %15 offset:1024\n\t"
-        "ds_read_b32 %7, %16 offset:1024\n\t"
-        "ds_read_b32 %8, %17 offset:1024\n\t"
-        "ds_read_b32 %9, %18 offset:1024\n\t"
-        "ds_read_b128 %10, %19\n\t"
-        "ds_read_b128 %11, %19 offset:64\n\t"
-        "ds_read_b128 %12, %19 offset:256\n\t"
-        "ds_read_b128 %13, %19 offset:320\n\t"
+        "ds_add_rtn_u32 %[cl], %[ca], %[one]\n\t"
+        "ds_read_b128 %[k00], %[ak0]\n\t"
+        "ds_read_b128 %[k10], %[ak0] offset:1024\n\t"
+        "ds_read_b32 %[v0], %[av0]\n\t"
+        "ds_read_b32 %[v1], %[av1]\n\t"
+        "ds_read_b32 %[v2], %[av2]\n\t"
+        "ds_read_b32 %[v3], %[av3]\n\t"
+        "ds_read_b32 %[v4], %[av0] offset:1024\n\t"
+        "ds_read_b32 %[v5], %[av1] offset:1024\n\t"
+        "ds_read_b32 %[v6], %[av2] offset:1024\n\t"
+        "ds_read_b32 %[v7], %[av3] offset:1024\n\t"
+        "ds_read_b128 %[ks0], %[as]\n\t"
+        "ds_read_b128 %[ks1], %[as] offset:64\n\t"
+        "ds_read_b128 %[vs0], %[as] offset:256\n\t"
+        "ds_read_b128 %[vs1], %[as] offset:320\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(t.k[0][0]), "=&v"(t.k[1][0]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]),
-          "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(t.ks[0]), "=&v"(t.ks[1]), "=&v"(t.vs[0]), "=&v"(t.vs[1])
-        : "v"(ak[0]), "v"(av[0]), "v"(av[1]), "v"(av[2]), "v"(av[3]), "v"(as));
+        : [k00] "=&v"(t.k[0][0]), [k10] "=&v"(t.k[1][0]), [v0] "=&v"(v[0]), [v1] "=&v"(v[1]), [v2] "=&v"(v[2]),
+          [v3] "=&v"(v[3]), [v4] "=&v"(v[4]), [v5] "=&v"(v[5]), [v6] "=&v"(v[6]), [v7] "=&v"(v[7]),
+          [ks0] "=&v"(t.ks[0]), [ks1] "=&v"(t.ks[1]), [vs0] "=&v"(t.vs[0]), [vs1] "=&v"(t.vs[1]),
+          [cl] "=&v"(claimed)
+        : [ak0] "v"(ak[0]), [av0] "v"(av[0]), [av1] "v"(av[1]), [av2] "v"(av[2]), [av3] "v"(av[3]),
+          [as] "v"(as), [ca] "v"(claim_addr), [one] "v"(one)
+        : "memory");
 #pragma unroll
     for (int i = 0; i < 8; ++i) t.v[i][0] = v[i];
   }
@@ -551,18 +566,6 @@ __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D /
   patch_new_row<D>(t, row_lds, ns, r, g, c);
 }
 
-// Atomic add on an LDS counter, returning the old value. Written out so the
-// compiler does not order it behind the staging loads in flight (it cannot
-// tell the counter from the slots those loads write, and would wait for all
-// of them before every claim); the asm waits for its own result.
-__device__ __forceinline__ int lds_fetch_add(int* counter, int v) {
-  const uint32_t addr =
-      (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)counter);
-  int old;
-  asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(old) : "v"(addr), "v"(v) : "memory");
-  return old;
-}
-
 // The work-group's tiles pt0 + [0, count) are handed out to its waves from an
 // LDS counter, so waves that run ahead (the SIMDs favour older waves) take
 // more tiles and all finish close together. Which wave sums which tile then
@@ -577,27 +580,22 @@ __device__ __forceinline__ int lds_fetch_add(int* counter, int v) {
 template <int D, int NT, bool Q8, typename Stage>
 __device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, WaveState<D, NT>& st,
                                           const Stage& stage, const QOperand<D, NT, Q8>& qop, float kscale,
-                                          int pt0, int count, int ia, int ib, int* next, int lane, int lo, int hi,
+                                          int pt0, int count, int ia, int ib, uint32_t claim_addr, int lane,
+                                          int lo, int hi,
                                           int g, int new_tile, const float (&xk)[D / 64], const float (&xv)[D / 64],
                                           int8_t* row_lds, bool write, int8_t* krow, int8_t* vrow, float* ks,
                                           float* vs, bool fixed) {
   constexpr int NDMA = Slot<D>::kDma;
   const int c = lane & 15;
-  // the next tile for the slot that holds tile i: the counter's, or with a
-  // fixed assignment the slot's next one (the wave's two slots alternate)
-  const auto claim = [&](int i) {
-    if (fixed) return i + 2 * kWavesPerWG;
-    int r = 0;
-    if (lane == 0) r = lds_fetch_add(next, 1);
-    return r;
-  };
   // One tile from `slot`: wait for its loads (only the other slot's may still
-  // be in flight), read it, refill the slot, compute.
-  const auto step = [&](char* slot, int& i, int claimed) {
+  // be in flight), read it and claim the slot's next tile (the counter's, or
+  // with a fixed assignment the slot's next one: the wave's two slots
+  // alternate), refill the slot, compute.
+  const auto step = [&](char* slot, int& i) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA));
-    read_slot<D>(cur, slot, g, c);
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the slot's reads (and the claim) are done
-    const int in = __builtin_amdgcn_readfirstlane(claimed);
+    int claimed;
+    read_slot<D>(cur, slot, g, c, claim_addr, claimed);
+    const int in = fixed ? i + 2 * kWavesPerWG : __builtin_amdgcn_readfirstlane(claimed);
     if (i == new_tile) {
       encode_new_row<D>(cur, xk, xv, row_lds, hi - 1 - (pt0 + i) * kTileKeys, g, c, lane, write, krow, vrow, ks,
                         vs);
@@ -612,9 +610,9 @@ __device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, Wave
   // ia < ib at the top of the loop and handed-out indices only grow, so once
   // ia is past the end so is ib (and vice versa in the middle).
   while (ia < count) {
-    step(s0, ia, claim(ia));
+    step(s0, ia);
     if (ib >= count) break;
-    step(s1, ib, claim(ib));
+    step(s1, ib);
   }
 }
 
@@ -650,6 +648,7 @@ void decode_partition_kernel(DecodeParams p) {
   __shared__ float sm_m[WV][HP];
   __shared__ float sm_l[WV][HP];
   __shared__ int sm_next;  // next tile (relative to pt0) to hand out
+  __shared__ int sm_dummy[kWave];  // targets of the claim adds of lanes other than 0
   __shared__ __attribute__((aligned(16))) int8_t sm_new[WV][2 * D];  // fused append: per-wave row buffer
   __shared__ int sm_tab[PAGED ? kMaxTableSlice : 1];  // physical blocks of the partition's tiles
 
@@ -835,7 +834,12 @@ void decode_partition_kernel(DecodeParams p) {
   st.vexp = -1000;
 
   Tile<D> cur;
-  run_tiles<D, NT, Q8>(s0, s1, cur, st, stage, qop, kscale, pt0, count, wave, wave + WV, &sm_next, lane, lo, hi, g,
+  const auto lds_addr = [](int* p_) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)p_);
+  };
+  const uint32_t claim_addr =
+      (lane == 0 && p.fixed_tiles == 0) ? lds_addr(&sm_next) : lds_addr(&sm_dummy[lane]);
+  run_tiles<D, NT, Q8>(s0, s1, cur, st, stage, qop, kscale, pt0, count, wave, wave + WV, claim_addr, lane, lo, hi, g,
                    new_tile, xk, xv, sm_new[wave], blockIdx.z == 0, p.k_w + new_row * D, p.v_w + new_row * D,
                    p.ks_w + new_row, p.vs_w + new_row, p.fixed_tiles != 0);
 
