@@ -222,7 +222,8 @@ def bench_hybrid(torch, m, acct, args, stream):
     res["global_kv_bytes"] = kv_layers[0]
     res["global_GBps"] = kv_layers[0] / (res["global_call"]["mean_us"] * 1e-6) / 1e9
     res["note"] = ("per-layer times are eager calls bracketed by events, each after a 1 GiB write (flushed) "
-                   "or after the block's previous layer; the block step is one graph replay")
+                   "or after the block's previous layer, so they include launch gaps the graph-replayed block "
+                   "step does not have; the block step is one graph replay")
     return res
 
 
