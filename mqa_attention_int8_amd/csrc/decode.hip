@@ -19,13 +19,18 @@
 //  * Eight waves per work-group, one work-group per compute unit. The
 //    work-group's tiles are handed to its waves from an LDS counter, so the
 //    waves finish together whatever the SIMD arbiter favours (which wave sums
-//    which tile, and so the last bits of the result, depends on timing).
+//    which tile, and so the last bits of the result, depends on timing; the
+//    deterministic setting assigns them in a fixed order instead).
+//  * Ragged batches (mqa_decode_ragged): a planner kernel cuts the list of
+//    all sequences' visible tiles into equal ranges, one per work-group; a
+//    work-group walks the sequence segments inside its range.
 //  * Per 32-key tile a wave runs S^T = K Q^T and O^T += V^T P''^T on fp16
 //    MFMA (v_mfma_f32_16x16x32_f16): 32 heads x 128 dims x 2 flops per key
 //    per product is far above what the vector ALUs can sustain at HBM rate.
 //  * int8 -> fp16 is exact and costs one instruction per element (an SDWA
-//    sign-extended byte convert). q is scaled per wave by a power of two into
-//    fp16's top binade; the scale is folded into the per-key logit factor.
+//    sign-extended byte convert, inline asm with its own MFMA wait states).
+//    q is scaled per wave by a power of two into fp16's top binade; the
+//    scale is folded into the per-key logit factor.
 //  * The contraction index d is permuted consistently in Q and K so that a
 //    lane's K bytes are one contiguous run of a key row; the key index is
 //    permuted consistently in P'' and V so that the accumulator layout of S^T
@@ -33,8 +38,11 @@
 //    column mapping makes each lane's V bytes contiguous within a row.
 //  * P'' (below) is split into fp16 hi + lo parts (two MFMAs), so the PV
 //    product carries 22 significant bits instead of 11.
-//  * Loads are software-pipelined: two tiles per wave in registers, one being
-//    computed while the other is in flight.
+//  * Loads are software-pipelined through LDS: each wave owns two slots that
+//    direct-to-LDS buffer loads fill (1 KB of contiguous rows per
+//    instruction); a slot is read into registers and refilled with the
+//    wave's next tile before that tile's arithmetic, so two tiles are in
+//    flight while one is computed.
 //  * Online softmax (running offset m, sum l, rescaled accumulator) in the
 //    log2 domain per head. The waves of a work-group combine through LDS.
 //    With several partitions per sequence, each work-group writes its
