@@ -184,6 +184,23 @@ struct Slot {
 // slot receives zeros).
 constexpr uint32_t kNowhere = 0x80000000u;
 
+// The tiles of a sequence's visible keys [lo, n): tile t covers rows
+// org + 32 t .. org + 32 t + 31 for t in [begin, end). A full window whose
+// length is a multiple of 32 (and a contiguous buffer: paged blocks need
+// aligned tiles) is tiled from its first key, so every tile is whole and
+// visible (1024 keys: 32 tiles instead of 33, none masked); otherwise tiles
+// are aligned to 32 rows and the first and last may be partly visible. Every
+// row of a tile lies below max(n, the aligned end) <= the cache capacity.
+struct TileRange {
+  int org, begin, end;
+};
+__device__ __forceinline__ TileRange tile_range(int n, int window, bool exact_ok) {
+  const int lo = window > 0 ? max(0, n - window) : 0;
+  if (exact_ok && window > 0 && window % kTileKeys == 0 && n >= window) return {lo, 0, window / kTileKeys};
+  const int b = lo / kTileKeys;
+  return {0, b, n > lo ? (n + kTileKeys - 1) / kTileKeys : b};
+}
+
 // Per-lane offsets of the staging loads: lane l of a 1 KB load takes chunk
 // (l % kCh) ^ (row % kCh) of row l / kCh of that kilobyte, so that LDS chunk
 // position p holds chunk (p % kCh) ^ (row % kCh) of row p / kCh.
@@ -574,7 +591,7 @@ __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D /
   patch_new_row<D>(t, row_lds, ns, r, g, c);
 }
 
-// The work-group's tiles pt0 + [0, count) are handed out to its waves from an
+// The work-group's tiles [0, count) (rows row0 + 32 i ..) are handed out to its waves from an
 // LDS counter, so waves that run ahead (the SIMDs favour older waves) take
 // more tiles and all finish close together. Which wave sums which tile then
 // depends on timing, so results can differ between runs in the last bits;
@@ -588,7 +605,7 @@ __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D /
 template <int D, int NT, bool Q8, typename Stage>
 __device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, WaveState<D, NT>& st,
                                           const Stage& stage, const QOperand<D, NT, Q8>& qop, float kscale,
-                                          int pt0, int count, int ia, int ib, uint32_t claim_addr, int lane,
+                                          int row0, int count, int ia, int ib, uint32_t claim_addr, int lane,
                                           int lo, int hi,
                                           int g, int new_tile, const float (&xk)[D / 64], const float (&xv)[D / 64],
                                           int8_t* row_lds, bool write, int8_t* krow, int8_t* vrow, float* ks,
@@ -605,14 +622,14 @@ __device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, Wave
     read_slot<D>(cur, slot, g, c, claim_addr, claimed);
     const int in = fixed ? i + 2 * kWavesPerWG : __builtin_amdgcn_readfirstlane(claimed);
     if (i == new_tile) {
-      encode_new_row<D>(cur, xk, xv, row_lds, hi - 1 - (pt0 + i) * kTileKeys, g, c, lane, write, krow, vrow, ks,
+      encode_new_row<D>(cur, xk, xv, row_lds, hi - 1 - (row0 + i * kTileKeys), g, c, lane, write, krow, vrow, ks,
                         vs);
       // the row's stores count with the staging loads: let them drain so the
       // counts above keep meaning "the other slot's loads"
       __builtin_amdgcn_s_waitcnt(0);
     }
     stage(slot, in);
-    compute_tile<D, NT, Q8>(cur, st, qop, kscale, (pt0 + i) * kTileKeys, lo, hi, g);
+    compute_tile<D, NT, Q8>(cur, st, qop, kscale, row0 + i * kTileKeys, lo, hi, g);
     i = in;
   };
   // ia < ib at the top of the loop and handed-out indices only grow, so once
@@ -655,7 +672,7 @@ void decode_partition_kernel(DecodeParams p) {
   };
   __shared__ float sm_m[WV][HP];
   __shared__ float sm_l[WV][HP];
-  __shared__ int sm_next;  // next tile (relative to pt0) to hand out
+  __shared__ int sm_next;  // next tile (relative to the partition's first) to hand out
   __shared__ int sm_dummy[kWave];  // targets of the claim adds of lanes other than 0
   __shared__ __attribute__((aligned(16))) int8_t sm_new[WV][2 * D];  // fused append: per-wave row buffer
   __shared__ int sm_tab[PAGED ? kMaxTableSlice : 1];  // physical blocks of the partition's tiles
@@ -756,13 +773,13 @@ void decode_partition_kernel(DecodeParams p) {
   n = n < 0 ? 0 : (n > p.max_len ? p.max_len : n);
   const int lo = WINDOWED ? max(0, n - p.window) : 0;
   const int hi = n;
-  const int t_begin = lo / kTileKeys;
-  const int t_end = hi > lo ? (hi + kTileKeys - 1) / kTileKeys : t_begin;
-  const int pt0 = t_begin + seg_lo;
-  const int pt1 = min(pt0 + seg_len, t_end);
+  const TileRange tr = tile_range(n, WINDOWED ? p.window : 0, !PAGED);
+  const int org = tr.org;  // row of tile 0 (0 unless a full window is tiled from its first key)
+  const int pt0 = tr.begin + seg_lo;
+  const int pt1 = min(pt0 + seg_len, tr.end);
   const int count = pt1 - pt0;  // tiles of this segment (may be <= 0)
   // Fused append: the wave that draws the tile holding row n - 1 encodes it.
-  const int new_tile = (appending && n > 0) ? (n - 1) / kTileKeys - pt0 : -1;  // outside [0, count): none here
+  const int new_tile = (appending && n > 0) ? (n - 1 - org) / kTileKeys - pt0 : -1;  // outside [0, count): none here
 
   // Paged: the physical blocks of this partition's tiles, read once into LDS
   // (entries clamped into the pool, so no access can leave it).
@@ -786,7 +803,7 @@ void decode_partition_kernel(DecodeParams p) {
   // Staging loads of tile i of the partition (i >= count: nothing is read).
   const auto stage = [&](char* slot, int i) {
     if (!PAGED) {
-      stage_tile<D>(slot, sb, lane_kv, lane_sc, (pt0 + i) * kTileKeys, i < count);
+      stage_tile<D>(slot, sb, lane_kv, lane_sc, org + (pt0 + i) * kTileKeys, i < count);
     } else {
       SeqBuffers tsb;
       const int64_t row = i < count ? phys_row((pt0 + i) * kTileKeys) : 0;
@@ -847,7 +864,8 @@ void decode_partition_kernel(DecodeParams p) {
   };
   const uint32_t claim_addr =
       (lane == 0 && p.fixed_tiles == 0) ? lds_addr(&sm_next) : lds_addr(&sm_dummy[lane]);
-  run_tiles<D, NT, Q8>(s0, s1, cur, st, stage, qop, kscale, pt0, count, wave, wave + WV, claim_addr, lane, lo, hi, g,
+  run_tiles<D, NT, Q8>(s0, s1, cur, st, stage, qop, kscale, org + pt0 * kTileKeys, count, wave, wave + WV, claim_addr,
+                       lane, lo, hi, g,
                    new_tile, xk, xv, sm_new[wave], blockIdx.z == 0, p.k_w + new_row * D, p.v_w + new_row * D,
                    p.ks_w + new_row, p.vs_w + new_row, p.fixed_tiles != 0);
 
@@ -1051,12 +1069,12 @@ __global__ __launch_bounds__(256 * kMergeMaxSlices) void decode_merge_kernel(con
 // ---------------------------------------------------------------------------
 constexpr int kMinChunk = kWavesPerWG;  // at least one tile per wave
 
+// The tiles the attention kernel computes for a sequence (balanced plans are
+// contiguous-buffer plans, so full windows are tiled from their first key).
 __device__ __forceinline__ int visible_tiles(int n, int window, int max_len) {
   n = n < 0 ? 0 : (n > max_len ? max_len : n);
-  const int lo = window > 0 ? max(0, n - window) : 0;
-  const int t_begin = lo / kTileKeys;
-  const int t_end = n > lo ? (n + kTileKeys - 1) / kTileKeys : t_begin;
-  return t_end - t_begin;
+  const TileRange tr = tile_range(n, window, true);
+  return tr.end - tr.begin;
 }
 
 // Inclusive prefix sum over the block; `total` receives the block's sum.

@@ -76,7 +76,7 @@ def run_case(wid, B, L, Hq, D, lens, window, what):
     assert_decode_close(out_a, ref, 1e-4, what)
 
 
-@pytest.mark.parametrize("window", [0, 100])
+@pytest.mark.parametrize("window", [0, 100, 64, 1024])
 def test_append_ragged(window):
     lens = [1, 2, 31, 32, 33, 500, 999, 1000]
     run_case(90, 8, 1000, 32, 128, lens, window, f"ragged W{window}")

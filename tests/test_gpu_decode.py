@@ -56,6 +56,16 @@ def test_windows_ragged(window):
     case(70, len(lens), 2100, 32, 128, lens, window, what=f"ragged W{window}")
 
 
+@pytest.mark.parametrize("window", [32, 64, 1024, 2048])
+def test_full_windows_tiled_from_their_first_key(window):
+    """A window of a multiple of 32 keys over a sequence at least that long is
+    tiled from its first key (no partly visible tiles); shorter sequences
+    keep 32-row-aligned tiles. Lengths on both sides of the switch."""
+    W = window
+    lens = [W - 1, W, W + 1, W + 17, W + 31, W + 32, W + 33, 3 * W + 5]
+    case(79, len(lens), 3 * W + 64, 32, 128, lens, W, what=f"full window W{W}")
+
+
 def test_empty_and_single():
     lens = [0, 1, 0, 2]
     case(71, 4, 64, 32, 128, lens, 0, max_len=64, what="empty/single")

@@ -44,7 +44,7 @@ def test_hybrid_global_layer_full():
     ragged_case(w.wid, w.B, L, w.Hq, w.D, lens, 0, "hybrid global layer")
 
 
-@pytest.mark.parametrize("window", [0, 100, 5000])
+@pytest.mark.parametrize("window", [0, 100, 5000, 4096])
 def test_mixed_lengths(window):
     lens = [0, 1, 31, 32, 33, 64, 1000, 4096, 20000, 7, 12345, 0, 3, 9000, 15000, 2]
     ragged_case(97, len(lens), 20000, 32, 128, lens, window, f"mixed W{window}")
