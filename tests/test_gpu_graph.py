@@ -103,3 +103,64 @@ def test_prefill_chunk_in_a_graph(window):
         m.mqa_prefill_chunk(q, kv, pl, int(plens.max()), window, out=out, workspace=ws)
 
     replay_and_check(calls, [out], [ref], lambda o, r, w: assert_prefill_close(o, r, what=w), 0.0)
+
+
+def test_ragged_decode_in_a_graph():
+    """The balanced plan in a graph: the planner kernel rewrites the plan in
+    the workspace on every replay (here after the workspace was overwritten
+    with garbage between replays), then the partitions and the merge read it.
+    Also the allocation-free call, whose states live in the library's
+    static array."""
+    import mqa_attention_int8_amd as m
+    B, Hq, D, L = 40, 32, 128, 6144
+    lens = synth.ragged_lens(synth.rng(43, synth.T_LENS), B, 0, L)
+    lens[0], lens[1] = L, 0
+    log(f"graph ragged decode: B={B} lens {lens.min()}..{lens.max()}")
+    hk = HostKV.seeded(43, 0, B, L, D)
+    knew = synth.normal_f32(synth.rng(43, synth.T_KNEW), (B, D))
+    vnew = synth.normal_f32(synth.rng(43, synth.T_VNEW), (B, D))
+    qg, qn = q_bits(43, (B, Hq, D), 0), q_bits(43, (B, Hq, D), 1)
+    kq, ks = oracle.quantize_rows(knew)
+    vq, vs = oracle.quantize_rows(vnew)
+    exp = [a.copy() for a in hk.arrays()]
+    for b in range(B):
+        r = int(lens[b]) - 1
+        if r >= 0:
+            exp[0][b, r], exp[1][b, r], exp[2][b, r], exp[3][b, r] = kq[b], ks[b], vq[b], vs[b]
+    refs = [oracle.decode_ref(qg, *exp, lens, 0), oracle.decode_ref(qn, *exp, lens, 0)]
+    kv = hk.to_device()
+    seq, kn, vn = dev(lens), dev(knew), dev(vnew)
+    q0, q1 = q_dev(qg), q_dev(qn)
+    outs = [torch.empty((B, Hq, D), device="cuda") for _ in range(2)]
+    ws = m.ragged_workspace(B, Hq, D, L, 0)
+
+    def calls():
+        m.mqa_decode_append_ragged(q0, kv, kn, vn, seq, L, 0, out=outs[0], workspace=ws)
+        m.mqa_decode_noalloc(q1, kv, seq, L, 0, out=outs[1])
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for o, r in zip(eager, refs):
+        assert_decode_close(o, r, 1e-4, "eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(REPLAYS):
+        ws.fill_(255)                                # the plan must be rebuilt by the replay
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, e, r) in enumerate(zip(outs, eager, refs)):
+            assert float((o - e).abs().max()) <= 1e-6, f"replay {rep} output {i}"
+            assert_decode_close(o, r, 1e-4, f"replay {rep} output {i}")
+    del g
+    got = [x.cpu().numpy() for x in (kv.k, kv.k_scale, kv.v, kv.v_scale)]
+    for g_, e in zip(got, exp):
+        assert np.array_equal(g_, e)
