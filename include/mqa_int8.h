@@ -193,16 +193,18 @@ size_t mqa_decode_ragged_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
  * ranges (from max_seq_len alone), so the compute units holding the longest
  * sequences finish last. Here a small planning kernel on the same stream
  * reads seq_lens and cuts the visible 32-key tiles of all sequences, taken in
- * order as one flat range, into equal ranges, one per work-group; a range
- * may end one sequence and start the next, and the partial softmax states of
+ * order as one flat range, into ranges of equal cost, one per work-group (a
+ * tile costs one unit and each sequence start a fixed 48, for the work of
+ * starting and ending a piece of a sequence); a range may end one sequence
+ * and start the next, and the partial softmax states of
  * every sequence are merged as in mqa_decode. A sliding window short enough
  * for mqa_decode's whole-window plan uses that plan (no planning kernel).
  * Results equal mqa_decode's up to the order of the floating-point sums.
  *   workspace  at least mqa_decode_ragged_workspace_bytes() bytes: the plan
  *              and the partial states (no initialisation needed).
  * Other arguments, layout and errors as mqa_decode; also MQA_ERR_SHAPE when
- * B * ceil(max_seq_len / 32) reaches 2^31 (the plan counts tiles in 32-bit
- * integers). */
+ * B * (ceil(max_seq_len / 32) + 49) reaches 2^31 (the plan counts tiles and
+ * sequence-start costs in 32-bit integers). */
 int mqa_decode_ragged(const uint16_t* q, const mqa_kv_view* kv,
                       const int32_t* seq_lens, int32_t max_seq_len, int32_t B,
                       int32_t Hq, int32_t D, int32_t window, float softmax_scale,

@@ -202,9 +202,10 @@ int mqa_decode_append(const uint16_t* q, const mqa_kv_cache* kv, const float* k_
 }
 
 namespace {
-// The balanced planner counts tiles in 32-bit integers.
+// The balanced planner counts tiles and sequence-start costs in 32-bit
+// integers.
 bool ragged_tiles_fit(int32_t B, int32_t max_seq_len) {
-  return (int64_t)B * (((int64_t)max_seq_len + 31) / 32 + 1) < ((int64_t)1 << 31);
+  return (int64_t)B * (((int64_t)max_seq_len + 31) / 32 + 1 + mqa::kRaggedSegmentCost) < ((int64_t)1 << 31);
 }
 
 int decode_ragged_impl(const uint16_t* q, const mqa_kv_view& view, const mqa_kv_cache* cache, const float* k_new,

@@ -22,8 +22,9 @@
 //    which tile, and so the last bits of the result, depends on timing; the
 //    deterministic setting assigns them in a fixed order instead).
 //  * Ragged batches (mqa_decode_ragged): a planner kernel cuts the list of
-//    all sequences' visible tiles into equal ranges, one per work-group; a
-//    work-group walks the sequence segments inside its range.
+//    all sequences' visible tiles into ranges of equal cost, one per
+//    work-group (a tile costs one unit, the start of a sequence a fixed
+//    number); a work-group walks the sequence segments inside its range.
 //  * Per 32-key tile a wave runs S^T = K Q^T and O^T += V^T P''^T on fp16
 //    MFMA (v_mfma_f32_16x16x32_f16): 32 heads x 128 dims x 2 flops per key
 //    per product is far above what the vector ALUs can sustain at HBM rate.
@@ -1052,22 +1053,32 @@ __global__ __launch_bounds__(256 * kMergeMaxSlices) void decode_merge_kernel(con
 // ---------------------------------------------------------------------------
 // Balanced plan of a ragged batch (one work-group of NTH threads: 256 for up
 // to 1024 sequences, measured ~1 us faster than 1024 there, else 1024).
-// The visible 32-key tiles of all sequences, in sequence order, form one
-// list of T tiles; with G the work-groups that fill the chip once, chunk
-// c = max(8, ceil(T / G)) and work-group j takes tiles [j c, (j + 1) c) of
-// the list, so exactly ceil(T / c) <= G work-groups have work and none has
-// more than c tiles, whatever the lengths. The part of sequence b that falls
-// in work-group j's range is a segment; a work-group's segments are
-// consecutive in (sequence, work-group) order, which is also the order of the
-// partial-state slots: sequence b (P_b tiles before it, t_b of its own)
-// spans work-groups P_b / c .. (P_b + t_b - 1) / c and owns that many
-// consecutive slots. Written (int32 words): header {c, T, segments,
-// work-groups with work}; per work-group (G) {first segment, segments};
-// per segment (at most G + B) {b, first tile, tiles, whole sequence?}; per
-// sequence (B) {first segment, segments}. Lengths are clamped exactly as the
-// attention kernel clamps them.
+// Work is counted in tile units: a sequence with t_b > 0 visible tiles costs
+// kSegmentCost + t_b, the first kSegmentCost units standing for the fixed
+// work of starting a segment (the length and q loads before its first tile,
+// the combine and state stores after its last). Laid end to end in sequence
+// order these costs form one line of C units; with G the work-groups that
+// fill the chip once, chunk c = max(8, ceil(C / G)) and work-group j takes
+// the tiles whose unit lies in [j c, (j + 1) c), so no work-group's tiles
+// plus the segment starts inside its range cost more than c, whatever the
+// lengths. (Equal tile counts alone left the work-groups that start several
+// short sequences well behind the rest.) Sequence b's tiles occupy units
+// A_b .. A_b + t_b - 1, A_b = Q_b + kSegmentCost with Q_b the cost of the
+// sequences before it; the part of it in work-group j's range is a segment;
+// a work-group's segments are consecutive in (sequence, work-group) order,
+// which is also the order of the partial-state slots: sequence b spans
+// work-groups A_b / c .. (A_b + t_b - 1) / c and owns that many consecutive
+// slots. Written (int32 words): header {c, T, segments, ceil(C / c)}; per
+// work-group (G) {first segment, segments} (segments = 0: no work, the first
+// word is then -1); per segment (at most G + B) {b, first tile, tiles, whole
+// sequence?}; per sequence (B) {first segment, segments}. Lengths are clamped
+// exactly as the attention kernel clamps them.
 // ---------------------------------------------------------------------------
 constexpr int kMinChunk = kWavesPerWG;  // at least one tile per wave
+// On the hybrid block's global layer (128 sequences of 1024..32768 keys, 256
+// work-groups) the call took 142, 134, 127, 125, 129 and 132 us with a
+// segment cost of 0, 16, 32, 48, 64 and 96 tiles.
+constexpr int kSegmentCost = kRaggedSegmentCost;
 
 // The tiles the attention kernel computes for a sequence (balanced plans are
 // contiguous-buffer plans, so full windows are tiled from their first key).
@@ -1076,6 +1087,7 @@ __device__ __forceinline__ int visible_tiles(int n, int window, int max_len) {
   const TileRange tr = tile_range(n, window, true);
   return tr.end - tr.begin;
 }
+__device__ __forceinline__ int sequence_cost(int t) { return t > 0 ? t + kSegmentCost : 0; }
 
 // Inclusive prefix sum over the block; `total` receives the block's sum.
 template <int NTH>
@@ -1110,51 +1122,66 @@ __global__ __launch_bounds__(NTH) void decode_plan_kernel(const int32_t* __restr
                                                                    int max_len, int G) {
   __shared__ int sm[NTH / 64];
   const int tid = threadIdx.x;
-  int part = 0;
-  for (int b = tid; b < B; b += NTH) part += visible_tiles(seq_lens[b], window, max_len);
-  int total;
-  (void)block_inclusive_sum<NTH>(part, sm, total);
-  const int chunk = (int)max<int64_t>(kMinChunk, ((int64_t)total + G - 1) / G);
-  const int busy = (int)(((int64_t)total + chunk - 1) / chunk);
+  int part_t = 0, part_c = 0;
+  for (int b = tid; b < B; b += NTH) {
+    const int t = visible_tiles(seq_lens[b], window, max_len);
+    part_t += t;
+    part_c += sequence_cost(t);
+  }
+  int total_t, total_c;
+  (void)block_inclusive_sum<NTH>(part_t, sm, total_t);
+  (void)block_inclusive_sum<NTH>(part_c, sm, total_c);
+  const int chunk = (int)max<int64_t>(kMinChunk, ((int64_t)total_c + G - 1) / G);
   int32_t* wg = plan + 4;
   int32_t* segs = plan + 4 + 2 * G;
   int32_t* seqs = segs + 4 * (G + B);
-  int carry_t = 0, carry_s = 0;
+  for (int j = tid; j < G; j += NTH) *reinterpret_cast<int2*>(wg + 2 * j) = make_int2(-1, 0);
+  __syncthreads();
+  int carry_c = 0, carry_s = 0;
   for (int base = 0; base < B; base += NTH) {
     const int b = base + tid;
     const int t = b < B ? visible_tiles(seq_lens[b], window, max_len) : 0;
-    int tot_t, tot_s;
-    const int P = carry_t + block_inclusive_sum<NTH>(t, sm, tot_t) - t;   // tiles before sequence b
-    const int j1 = P / chunk, j2 = (int)(((int64_t)P + t - 1) / chunk);
+    const int cost = sequence_cost(t);
+    int tot_c, tot_s;
+    const int Q = carry_c + block_inclusive_sum<NTH>(cost, sm, tot_c) - cost;  // cost of the sequences before b
+    const int A = Q + kSegmentCost;                                              // unit of its first tile
+    const int j1 = A / chunk, j2 = (int)(((int64_t)A + t - 1) / chunk);
     const int n = t > 0 ? j2 - j1 + 1 : 0;
     const int S = carry_s + block_inclusive_sum<NTH>(n, sm, tot_s) - n;  // segments before sequence b
     if (b < B) {
       *reinterpret_cast<int2*>(seqs + 2 * b) = make_int2(S, n);
+      // the previous sequence with tiles ends at unit Q - 1: is it in j1's range?
+      const bool shares_j1 = Q > 0 && (Q - 1) / chunk == j1;
       for (int k = 0; k < n; ++k) {
         const int j = j1 + k;
         const int64_t start = (int64_t)j * chunk;  // 64-bit: (j + 1) c may pass 2^31
-        const int lo = (int)max(start, (int64_t)P), hi = (int)min(start + chunk, (int64_t)P + t);
-        *reinterpret_cast<int4*>(segs + 4 * (S + k)) = make_int4(b, lo - P, hi - lo, n == 1);
-        if (lo == start) wg[2 * j] = S + k;  // the segment that starts work-group j's range
+        const int lo = (int)max(start, (int64_t)A), hi = (int)min(start + chunk, (int64_t)A + t);
+        *reinterpret_cast<int4*>(segs + 4 * (S + k)) = make_int4(b, lo - A, hi - lo, n == 1);
+        if (k > 0 || !shares_j1) wg[2 * j] = S + k;  // the first segment of work-group j's range
       }
     }
-    carry_t += tot_t;
+    carry_c += tot_c;
     carry_s += tot_s;
   }
-  __syncthreads();  // every busy work-group's first segment is written
+  __syncthreads();  // every work-group's first segment is written
   for (int j = tid; j < G; j += NTH) {
-    if (j < busy) {
-      const int next = j + 1 < busy ? wg[2 * (j + 1)] : carry_s;
-      wg[2 * j + 1] = next - wg[2 * j];
-    } else {
-      *reinterpret_cast<int2*>(wg + 2 * j) = make_int2(0, 0);
+    const int first = wg[2 * j];
+    if (first < 0) continue;  // no tile in this range
+    int next = carry_s;
+    for (int i = j + 1; i < G; ++i) {
+      const int f = wg[2 * i];
+      if (f >= 0) {
+        next = f;
+        break;
+      }
     }
+    wg[2 * j + 1] = next - first;
   }
   if (tid == 0) {
     plan[0] = chunk;
-    plan[1] = total;
+    plan[1] = total_t;
     plan[2] = carry_s;
-    plan[3] = busy;
+    plan[3] = (int)(((int64_t)total_c + chunk - 1) / chunk);
   }
 }
 

@@ -37,10 +37,14 @@ DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, in
                        int num_cus, int32_t block_size = 0);
 // Balanced plan for a batch of ragged lengths (contiguous buffers, bf16
 // queries): a planner kernel splits the visible tiles of all sequences into
-// equal ranges per work-group; windows short enough for the whole-range plan
-// keep it (ragged_groups == 0 then).
+// ranges of equal cost per work-group (tiles plus a fixed cost per sequence
+// start); windows short enough for the whole-range plan keep it
+// (ragged_groups == 0 then).
 DecodePlan plan_decode_ragged(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_len, int32_t window,
                               int num_cus);
+// Cost of a sequence start in the balanced plan, in tiles (the plan cuts
+// tiles plus these costs into equal ranges).
+constexpr int kRaggedSegmentCost = 48;
 
 int launch_quantize(const float* src, int8_t* dst, float* dst_scale, const int32_t* start_pos,
                     int32_t B, int32_t T, int32_t D, int32_t L_cap, hipStream_t stream);

@@ -1,8 +1,9 @@
 """mqa_decode_ragged / mqa_decode_append_ragged (a planning kernel cuts the
-list of all sequences' visible tiles into ranges of at most max(8, ceil(T / G))
-tiles, one per work-group, which walks the sequence segments inside its
-range) against the oracle, and against mqa_decode on the same inputs (the
-same arithmetic summed in another order)."""
+list of all sequences' visible tiles into ranges of equal cost, a tile
+costing one unit and a sequence start a fixed number, one per work-group,
+which walks the sequence segments inside its range) against the oracle, and
+against mqa_decode on the same inputs (the same arithmetic summed in another
+order); the plan itself against a host model of its documented layout."""
 import numpy as np
 import pytest
 import torch
@@ -111,3 +112,44 @@ def test_append_ragged_hybrid_global():
             f"cache {name} differs from the oracle encoding"
     ref = oracle.decode_ref(qb, *exp, lens, 0)
     assert_decode_close(out, ref, 1e-4, "append ragged vs oracle")
+
+
+@pytest.mark.parametrize("case", ["hybrid", "mixed_w4096", "2500", "sparse"])
+def test_plan_words_match_the_model(case):
+    """The planning kernel's words (start of the workspace, which is filled
+    with 0xff first) against the host model of the documented layout; the
+    segment slots past the last used one are not compared."""
+    import mqa_attention_int8_amd as m
+    from plan_model import n_words, plan_words, unpack
+    window, Hq, D = 0, 32, 128
+    if case == "hybrid":
+        lens = synth.HYBRID.lens()
+    elif case == "mixed_w4096":
+        lens, window = np.array([0, 1, 31, 32, 33, 64, 1000, 4096, 20000, 7, 12345, 0, 3, 9000, 15000, 2]), 4096
+    elif case == "2500":
+        lens, Hq, D = synth.ragged_lens(synth.rng(103, synth.T_LENS), 2500, 0, 700), 8, 64
+    else:   # few tiles: most work-groups' ranges hold only sequence-start cost
+        lens = np.array([40, 3000, 0, 5, 0, 0, 700])
+    lens = np.asarray(lens, np.int32)
+    B, L = len(lens), int(lens.max())
+    Lc = (L + 31) // 32 * 32
+    G = torch.cuda.get_device_properties(0).multi_processor_count // ((Hq + 31) // 32)
+    log(f"plan words {case}: B={B} G={G} W={window}")
+    kv = m.KVView.empty(B, Lc, D)
+    for t in (kv.k, kv.v):
+        t.zero_()
+    kv.k_scale.fill_(1.0)
+    kv.v_scale.fill_(1.0)
+    ws = m.ragged_workspace(B, Hq, D, L, window)
+    ws.fill_(255)
+    q = torch.zeros((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    m.mqa_decode_ragged(q, kv, dev(lens), L, window, workspace=ws)
+    torch.cuda.synchronize()
+    got = ws[:4 * n_words(G, B)].view(torch.int32).cpu().numpy()
+    want, S = plan_words(lens, window, L, G)
+    gh, gw, gs, gq = unpack(got, G, B)
+    wh, ww, ws_, wq = unpack(want, G, B)
+    assert np.array_equal(gh, wh), (gh, wh)
+    assert np.array_equal(gw, ww)
+    assert np.array_equal(gs[:S], ws_[:S])
+    assert np.array_equal(gq, wq)
