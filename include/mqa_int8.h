@@ -194,7 +194,7 @@ size_t mqa_decode_ragged_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
  * sequences finish last. Here a small planning kernel on the same stream
  * reads seq_lens and cuts the visible 32-key tiles of all sequences, taken in
  * order as one flat range, into ranges of equal cost, one per work-group (a
- * tile costs one unit and each sequence start a fixed 48, for the work of
+ * tile costs one unit and each sequence start a fixed 40, for the work of
  * starting and ending a piece of a sequence); a range may end one sequence
  * and start the next, and the partial softmax states of
  * every sequence are merged as in mqa_decode. A sliding window short enough
@@ -203,7 +203,7 @@ size_t mqa_decode_ragged_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
  *   workspace  at least mqa_decode_ragged_workspace_bytes() bytes: the plan
  *              and the partial states (no initialisation needed).
  * Other arguments, layout and errors as mqa_decode; also MQA_ERR_SHAPE when
- * B * (ceil(max_seq_len / 32) + 49) reaches 2^31 (the plan counts tiles and
+ * B * (ceil(max_seq_len / 32) + 41) reaches 2^31 (the plan counts tiles and
  * sequence-start costs in 32-bit integers). */
 int mqa_decode_ragged(const uint16_t* q, const mqa_kv_view* kv,
                       const int32_t* seq_lens, int32_t max_seq_len, int32_t B,

@@ -599,10 +599,14 @@ __device__ __forceinline__ void encode_new_row(Tile<D>& t, const float (&xk)[D /
 // with `fixed` (the deterministic setting) wave w takes tiles w, w + 8, ...
 // instead, and every sum has a fixed order.
 // Each wave stages two tiles in its LDS slots: on entry s0 receives its tile
-// ia and s1 its tile ib (> ia). A slot is read into the register tile, then
-// refilled with the next handed-out tile (claimed before the read, so the
-// counter's round trip overlaps it) before the arithmetic of the tile just
-// read, so two tiles are always on their way from memory.
+// ia and s1 its tile ib (> ia). A slot is read into the register tile (and
+// the slot's next tile claimed in the same LDS round trip), the tile is
+// computed, then the slot is refilled: one tile per wave is in flight while
+// it computes, two while it waits. (Refilling before the arithmetic, with two
+// tiles always in flight, measured ~1 us slower on a 64 x 4096-key global
+// call and ~2 us on 8 x 131072 keys: the chip then holds ~36 MB of requests,
+// and every load, a segment's q rows and first tiles included, queues behind
+// them.)
 template <int D, int NT, bool Q8, typename Stage>
 __device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, WaveState<D, NT>& st,
                                           const Stage& stage, const QOperand<D, NT, Q8>& qop, float kscale,
@@ -616,7 +620,7 @@ __device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, Wave
   // One tile from `slot`: wait for its loads (only the other slot's may still
   // be in flight), read it and claim the slot's next tile (the counter's, or
   // with a fixed assignment the slot's next one: the wave's two slots
-  // alternate), refill the slot, compute.
+  // alternate), compute, refill the slot.
   const auto step = [&](char* slot, int& i) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(NDMA));
     int claimed;
@@ -629,8 +633,8 @@ __device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, Wave
       // counts above keep meaning "the other slot's loads"
       __builtin_amdgcn_s_waitcnt(0);
     }
-    stage(slot, in);
     compute_tile<D, NT, Q8>(cur, st, qop, kscale, row0 + i * kTileKeys, lo, hi, g);
+    stage(slot, in);
     i = in;
   };
   // ia < ib at the top of the loop and handed-out indices only grow, so once
@@ -693,8 +697,10 @@ void decode_partition_kernel(DecodeParams p) {
   // (relative to the first visible tile; tiles past the visible range are
   // dropped). The states go to partial-state slot `slot`, or straight to the
   // output when the segment is the whole sequence (`direct`).
+  // (n_plan: the sequence's clamped length as the balanced plan recorded it;
+  // other plans load it here.)
   const auto segment = [&](const int b, const int seg_lo, const int seg_len, const int64_t slot,
-                           const bool direct) {
+                           const bool direct, const int n_plan) {
   // Contiguous layout: one buffer resource per tensor of this sequence (the
   // rows of tiles past the length but inside the capacity are masked).
   // Paged layout: resources are made per tile (below).
@@ -717,7 +723,9 @@ void decode_partition_kernel(DecodeParams p) {
   // The length goes through the vector memory path: a scalar load would be
   // waited for at the barrier below (it shares a counter with the LDS write
   // before it).
-  const int n_raw = (int)buf_load4(make_rsrc(p.seq_lens + b, 4), 0, 0);
+  int n_raw;
+  if constexpr (RAGGED) n_raw = n_plan;
+  else n_raw = (int)buf_load4(make_rsrc(p.seq_lens + b, 4), 0, 0);
   u32x4 qraw[NT][KK];
   QOperand<D, NT, Q8> qop;
   if constexpr (!Q8) {
@@ -762,7 +770,7 @@ void decode_partition_kernel(DecodeParams p) {
   // delay the q loads of those dispatched last.)
   char* const s0 = sm_s0[wave];
   char* const s1 = sm_s1[wave];
-  if (!WINDOWED && !PAGED) {
+  if (!WINDOWED && !PAGED && !RAGGED) {
     const int t0 = seg_lo + wave;
     stage_tile<D>(s0, sb, lane_kv, lane_sc, t0 * kTileKeys, wave < seg_len && (t0 + 1) * kTileKeys <= p.L_cap);
   }
@@ -816,7 +824,7 @@ void decode_partition_kernel(DecodeParams p) {
       stage_tile<D>(slot, tsb, lane_kv, lane_sc, 0, i < count);
     }
   };
-  if (WINDOWED || PAGED) stage(s0, wave);
+  if (WINDOWED || PAGED || RAGGED) stage(s0, wave);
   stage(s1, wave + WV);
 
   // Q^T as the B operand in fp16: the wave scales q by an exact power of two
@@ -945,7 +953,7 @@ void decode_partition_kernel(DecodeParams p) {
 
   if constexpr (!RAGGED) {
     const int part = blockIdx.x, tpp = p.tiles_per_part;
-    segment(blockIdx.y, part * tpp, tpp, (int64_t)blockIdx.y * p.num_parts + part, p.num_parts == 1);
+    segment(blockIdx.y, part * tpp, tpp, (int64_t)blockIdx.y * p.num_parts + part, p.num_parts == 1, 0);
   } else {
     // the segments of this work-group's range of the balanced plan, in order
     // (each segment begins with a barrier, so the previous one's combine is
@@ -956,8 +964,12 @@ void decode_partition_kernel(DecodeParams p) {
     const int32_t* segs = p.plan + 4 + 2 * p.plan_G;
     for (int k = 0; k < nseg; ++k) {
       const int4 sg = *reinterpret_cast<const int4*>(segs + 4 * (first + k));
-      segment(__builtin_amdgcn_readfirstlane(sg.x), __builtin_amdgcn_readfirstlane(sg.y),
-              __builtin_amdgcn_readfirstlane(sg.z), (int64_t)(first + k), __builtin_amdgcn_readfirstlane(sg.w) != 0);
+      const int seg_lo = __builtin_amdgcn_readfirstlane(sg.y), seg_len = __builtin_amdgcn_readfirstlane(sg.z);
+      const int n = __builtin_amdgcn_readfirstlane(sg.w);
+      // a segment holding all of the sequence's tiles writes the output directly
+      const TileRange tr = tile_range(n, WINDOWED ? p.window : 0, true);
+      segment(__builtin_amdgcn_readfirstlane(sg.x), seg_lo, seg_len, (int64_t)(first + k),
+              seg_lo == 0 && seg_len == tr.end - tr.begin, n);
     }
   }
 }
@@ -1070,14 +1082,17 @@ __global__ __launch_bounds__(256 * kMergeMaxSlices) void decode_merge_kernel(con
 // work-groups A_b / c .. (A_b + t_b - 1) / c and owns that many consecutive
 // slots. Written (int32 words): header {c, T, segments, ceil(C / c)}; per
 // work-group (G) {first segment, segments} (segments = 0: no work, the first
-// word is then -1); per segment (at most G + B) {b, first tile, tiles, whole
-// sequence?}; per sequence (B) {first segment, segments}. Lengths are clamped
-// exactly as the attention kernel clamps them.
+// word is then -1); per segment (at most G + B) {b, first tile, tiles, length
+// of b}; per sequence (B) {first segment, segments}. Lengths are clamped to
+// [0, max_len] as the attention kernel clamps them; the attention kernel takes
+// a segment's length from the plan, so its first tiles go out at once.
 // ---------------------------------------------------------------------------
 constexpr int kMinChunk = kWavesPerWG;  // at least one tile per wave
 // On the hybrid block's global layer (128 sequences of 1024..32768 keys, 256
 // work-groups) the call took 142, 134, 127, 125, 129 and 132 us with a
-// segment cost of 0, 16, 32, 48, 64 and 96 tiles.
+// segment cost of 0, 16, 32, 48, 64 and 96 tiles; once a segment's length
+// came from the plan and its first tiles went out at once, 40 measured
+// ~2.7 us faster than 48 (and 32 ~1 us, 24 no faster).
 constexpr int kSegmentCost = kRaggedSegmentCost;
 
 // The tiles the attention kernel computes for a sequence (balanced plans are
@@ -1140,7 +1155,8 @@ __global__ __launch_bounds__(NTH) void decode_plan_kernel(const int32_t* __restr
   int carry_c = 0, carry_s = 0;
   for (int base = 0; base < B; base += NTH) {
     const int b = base + tid;
-    const int t = b < B ? visible_tiles(seq_lens[b], window, max_len) : 0;
+    const int nb = b < B ? min(max(seq_lens[b], 0), max_len) : 0;   // clamped as the attention kernel clamps
+    const int t = visible_tiles(nb, window, max_len);
     const int cost = sequence_cost(t);
     int tot_c, tot_s;
     const int Q = carry_c + block_inclusive_sum<NTH>(cost, sm, tot_c) - cost;  // cost of the sequences before b
@@ -1156,7 +1172,7 @@ __global__ __launch_bounds__(NTH) void decode_plan_kernel(const int32_t* __restr
         const int j = j1 + k;
         const int64_t start = (int64_t)j * chunk;  // 64-bit: (j + 1) c may pass 2^31
         const int lo = (int)max(start, (int64_t)A), hi = (int)min(start + chunk, (int64_t)A + t);
-        *reinterpret_cast<int4*>(segs + 4 * (S + k)) = make_int4(b, lo - A, hi - lo, n == 1);
+        *reinterpret_cast<int4*>(segs + 4 * (S + k)) = make_int4(b, lo - A, hi - lo, nb);
         if (k > 0 || !shares_j1) wg[2 * j] = S + k;  // the first segment of work-group j's range
       }
     }

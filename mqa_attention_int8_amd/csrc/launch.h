@@ -44,7 +44,7 @@ DecodePlan plan_decode_ragged(int32_t B, int32_t Hq, int32_t D, int32_t max_seq_
                               int num_cus);
 // Cost of a sequence start in the balanced plan, in tiles (the plan cuts
 // tiles plus these costs into equal ranges).
-constexpr int kRaggedSegmentCost = 48;
+constexpr int kRaggedSegmentCost = 40;
 
 int launch_quantize(const float* src, int8_t* dst, float* dst_scale, const int32_t* start_pos,
                     int32_t B, int32_t T, int32_t D, int32_t L_cap, hipStream_t stream);

@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import numpy as np
 
-SEGMENT_COST = 48   # cost of a sequence start, in tiles
+SEGMENT_COST = 40   # cost of a sequence start, in tiles
 MIN_CHUNK = 8       # at least one tile per wave of a work-group
 TILE = 32
 
@@ -33,8 +33,8 @@ def plan_words(seq_lens, window: int, max_len: int, G: int) -> np.ndarray:
     """The plan as int32 words: header {chunk, T, segments, ranges used};
     per work-group {first segment, segments} ({-1, 0} without tiles); per
     segment slot (G + B of them, unused ones left as they were: zero here)
-    {sequence, first tile, tiles, whole sequence?}; per sequence {first
-    segment, segments}."""
+    {sequence, first tile, tiles, the sequence's length clamped to
+    [0, max_len]}; per sequence {first segment, segments}."""
     B = len(seq_lens)
     tiles = [visible_tiles(int(n), window, max_len) for n in seq_lens]
     cost = [t + SEGMENT_COST if t > 0 else 0 for t in tiles]
@@ -52,7 +52,7 @@ def plan_words(seq_lens, window: int, max_len: int, G: int) -> np.ndarray:
         for k in range(n):
             j = A // chunk + k
             lo, hi = max(j * chunk, A), min((j + 1) * chunk, A + t)
-            segs[S + k] = (b, lo - A, hi - lo, int(n == 1))
+            segs[S + k] = (b, lo - A, hi - lo, min(max(int(seq_lens[b]), 0), max_len))
             # first segment of range j: a range that opens inside this sequence,
             # or one where no earlier sequence has a tile
             if k > 0 or Q == 0 or (Q - 1) // chunk != j:

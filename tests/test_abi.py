@@ -172,10 +172,10 @@ def test_workspace_sizes(lib):
         assert n == 0 or n >= 2 * B * Hq * (D + 2) * 4
     assert m.mqa_decode_workspace_bytes(8, 32, 128, 131072, 0) > 0
     assert m.mqa_decode_workspace_bytes(0, 32, 128, 4096, 0) == 0      # invalid -> 0
-    # the balanced plan counts tiles plus 48 per sequence start in 32-bit
-    # integers: B * (ceil(L / 32) + 1 + 48) must stay below 2^31
-    assert m.mqa_decode_ragged_workspace_bytes(65535, 8, 64, 32719 * 32, 0) > 0
-    assert m.mqa_decode_ragged_workspace_bytes(65535, 8, 64, 32719 * 32 + 1, 0) == 0
+    # the balanced plan counts tiles plus 40 per sequence start in 32-bit
+    # integers: B * (ceil(L / 32) + 1 + 40) must stay below 2^31
+    assert m.mqa_decode_ragged_workspace_bytes(65535, 8, 64, 32727 * 32, 0) > 0
+    assert m.mqa_decode_ragged_workspace_bytes(65535, 8, 64, 32727 * 32 + 1, 0) == 0
 
 
 def test_accounting_matches_oracle():

@@ -46,7 +46,7 @@ def check(lens, window, max_len, G):
         assert n >= 0 and (n > 0) == (first >= 0)
         cost = 0
         for s in range(first, first + n):
-            b, lo, ln, whole = segs[s]
+            b, lo, ln, length = segs[s]
             assert ln > 0 and 0 <= lo and lo + ln <= tiles[b]
             for x in range(lo, lo + ln):
                 assert (b, x) not in owner
@@ -63,7 +63,7 @@ def check(lens, window, max_len, G):
             assert sorted(set(js)) == list(range(min(js), max(js) + 1)) and len(set(js)) == n
             assert all(segs[first + k][0] == b for k in range(n))
             assert [segs[first + k][1] for k in range(n)] == sorted(segs[first + k][1] for k in range(n))
-            assert all(segs[first + k][3] == (n == 1) for k in range(n))
+            assert all(segs[first + k][3] == min(max(int(lens[b]), 0), max_len) for k in range(n))
         else:
             assert n == 0
 
@@ -84,7 +84,7 @@ def test_hybrid_global_layer():
 
 def test_sequence_starts_shift_work_off_busy_ranges():
     """Ranges that start several short sequences get fewer tiles: the cost of
-    a range (tiles plus 48 per sequence start) stays within one chunk of the
+    a range (tiles plus 40 per sequence start) stays within one chunk of the
     others'."""
     lens = [32 * 300] * 10 + [32 * 20] * 30 + [32 * 300] * 10
     B, G = len(lens), 16
