@@ -191,13 +191,14 @@ size_t mqa_decode_ragged_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
  * dialog's whole history; "秘訣2": dialogs are long and of very different
  * lengths.] mqa_decode splits every sequence into the same number of key
  * ranges (from max_seq_len alone), so the compute units holding the longest
- * sequences finish last. Here a small planning kernel on the same stream
- * reads seq_lens and cuts the visible 32-key tiles of all sequences, taken in
- * order as one flat range, into ranges of equal cost, one per work-group (a
- * tile costs one unit and each sequence start a fixed 40, for the work of
- * starting and ending a piece of a sequence); a range may end one sequence
- * and start the next, and the partial softmax states of
- * every sequence are merged as in mqa_decode. A sliding window short enough
+ * sequences finish last. Here seq_lens is read on the device (by every
+ * work-group of the attention kernel for up to 512 sequences, else by a
+ * small planning kernel on the same stream), and the visible 32-key tiles
+ * of all sequences, taken in order as one flat range, are cut into ranges
+ * of equal cost, one per work-group (a tile costs one unit and each
+ * sequence start a fixed 40, for the work of starting and ending a piece of
+ * a sequence); a range may end one sequence and start the next, and the
+ * partial softmax states of every sequence are merged as in mqa_decode. A sliding window short enough
  * for mqa_decode's whole-window plan uses that plan (no planning kernel).
  * Results equal mqa_decode's up to the order of the floating-point sums.
  *   workspace  at least mqa_decode_ragged_workspace_bytes() bytes: the plan

@@ -129,8 +129,9 @@ struct DecodeParams {
   float2* ws_ml;     // [slots, Hq] (offset m in log2 units, sum l of 2^(z - m))
   // Balanced plan of a ragged batch, written by decode_plan_kernel (layout
   // there); plan_G work-groups per head group.
-  const int32_t* plan;
+  int32_t* plan;
   int32_t plan_G;
+  int32_t plan_inline;      // != 0: each work-group derives its own range of the plan (B <= kInlinePlanMaxB)
   int32_t fixed_tiles;      // != 0: wave w takes tiles w, w + 8, ... (bitwise repeatable)
   int32_t B;
   int32_t L_cap;
@@ -646,6 +647,83 @@ __device__ __forceinline__ void run_tiles(char* s0, char* s1, Tile<D>& cur, Wave
   }
 }
 
+// ---------------------------------------------------------------------------
+// Balanced plan of a ragged batch: up to kInlinePlanMaxB sequences each
+// work-group of the attention kernel derives its own part of it; larger
+// batches get it from decode_plan_kernel (one work-group of NTH threads: 256
+// up to 1024 sequences, measured ~1 us faster than 1024 there, else 1024).
+// Work is counted in tile units: a sequence with t_b > 0 visible tiles costs
+// kSegmentCost + t_b, the first kSegmentCost units standing for the fixed
+// work of starting a segment (the length and q loads before its first tile,
+// the combine and state stores after its last). Laid end to end in sequence
+// order these costs form one line of C units; with G the work-groups that
+// fill the chip once, chunk c = max(8, ceil(C / G)) and work-group j takes
+// the tiles whose unit lies in [j c, (j + 1) c), so no work-group's tiles
+// plus the segment starts inside its range cost more than c, whatever the
+// lengths. (Equal tile counts alone left the work-groups that start several
+// short sequences well behind the rest.) Sequence b's tiles occupy units
+// A_b .. A_b + t_b - 1, A_b = Q_b + kSegmentCost with Q_b the cost of the
+// sequences before it; the part of it in work-group j's range is a segment;
+// a work-group's segments are consecutive in (sequence, work-group) order,
+// which is also the order of the partial-state slots: sequence b spans
+// work-groups A_b / c .. (A_b + t_b - 1) / c and owns that many consecutive
+// slots. Written (int32 words): header {c, T, segments, ceil(C / c)}; per
+// work-group (G) {first segment, segments} (segments = 0: no work, the first
+// word is then -1); per segment (at most G + B) {b, first tile, tiles, length
+// of b}; per sequence (B) {first segment, segments}. Lengths are clamped to
+// [0, max_len] as the attention kernel clamps them; the attention kernel takes
+// a segment's length from the plan, so its first tiles go out at once.
+// ---------------------------------------------------------------------------
+constexpr int kMinChunk = kWavesPerWG;  // at least one tile per wave
+// Batches up to this size are planned inside the attention kernel (one
+// sequence per thread of a work-group; no planning kernel, whose launch and
+// round trips cost ~5 us per call); larger ones by decode_plan_kernel.
+constexpr int kInlinePlanMaxB = 64 * kWavesPerWG;
+// On the hybrid block's global layer (128 sequences of 1024..32768 keys, 256
+// work-groups) the call took 142, 134, 127, 125, 129 and 132 us with a
+// segment cost of 0, 16, 32, 48, 64 and 96 tiles; once a segment's length
+// came from the plan and its first tiles went out at once, 40 measured
+// ~2.7 us faster than 48 (and 32 ~1 us, 24 no faster).
+constexpr int kSegmentCost = kRaggedSegmentCost;
+
+// The tiles the attention kernel computes for a sequence (balanced plans are
+// contiguous-buffer plans, so full windows are tiled from their first key).
+__device__ __forceinline__ int visible_tiles(int n, int window, int max_len) {
+  n = n < 0 ? 0 : (n > max_len ? max_len : n);
+  const TileRange tr = tile_range(n, window, true);
+  return tr.end - tr.begin;
+}
+__device__ __forceinline__ int sequence_cost(int t) { return t > 0 ? t + kSegmentCost : 0; }
+// Words of the balanced plan's area (layout above).
+__host__ __device__ constexpr size_t ragged_plan_words(size_t G, size_t B) { return 4 + 2 * G + 4 * (G + B) + 2 * B; }
+
+// Inclusive prefix sum over the block; `total` receives the block's sum.
+template <int NTH>
+__device__ __forceinline__ int block_inclusive_sum(int v, int* sm, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) sm[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    int x = lane < NTH / 64 ? sm[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < NTH / 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane < NTH / 64) sm[lane] = x;
+  }
+  __syncthreads();
+  const int add = w > 0 ? sm[w - 1] : 0;
+  total = sm[NTH / 64 - 1];
+  __syncthreads();  // sm is reused by the next call
+  return v + add;
+}
+
 // WINDOWED: the layer attends to the last `window` keys (the partition's
 // tiles then depend on the sequence length); otherwise to all of them.
 // PAGED: the cache is a block pool addressed through p.table.
@@ -681,6 +759,10 @@ void decode_partition_kernel(DecodeParams p) {
   __shared__ int sm_dummy[kWave];  // targets of the claim adds of lanes other than 0
   __shared__ __attribute__((aligned(16))) int8_t sm_new[WV][2 * D];  // fused append: per-wave row buffer
   __shared__ int sm_tab[PAGED ? kMaxTableSlice : 1];  // physical blocks of the partition's tiles
+  // Balanced plan derived in the kernel: this work-group's segments.
+  __shared__ int4 sm_plan_segs[RAGGED ? kInlinePlanMaxB : 1];
+  __shared__ int sm_plan_scan[kWavesPerWG];
+  __shared__ int sm_plan_first, sm_plan_n;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -958,12 +1040,59 @@ void decode_partition_kernel(DecodeParams p) {
     // the segments of this work-group's range of the balanced plan, in order
     // (each segment begins with a barrier, so the previous one's combine is
     // over before its LDS is reused)
-    const int2 wg = *reinterpret_cast<const int2*>(p.plan + 4 + 2 * blockIdx.x);
-    const int first = __builtin_amdgcn_readfirstlane(wg.x);
-    const int nseg = __builtin_amdgcn_readfirstlane(wg.y);
-    const int32_t* segs = p.plan + 4 + 2 * p.plan_G;
+    int first, nseg, seg0;
+    const int4* segs;
+    if (p.plan_inline) {
+      // This work-group's range of the plan decode_plan_kernel would write
+      // (same integer arithmetic, one sequence per thread): its segments go
+      // to LDS, and the per-sequence words the merge kernel reads are written
+      // by the work-group holding each sequence's first segment (work-group 0
+      // for sequences with no visible tile).
+      const int b = threadIdx.x;
+      const int nb = b < p.B ? min(max(p.seq_lens[b], 0), p.max_len) : 0;
+      const int t = b < p.B ? visible_tiles(nb, WINDOWED ? p.window : 0, p.max_len) : 0;
+      const int cost = sequence_cost(t);
+      if (threadIdx.x == 0) {
+        sm_plan_first = 0x7fffffff;
+        sm_plan_n = 0;
+      }
+      int total_c, total_s;
+      const int Q = block_inclusive_sum<NTHR>(cost, sm_plan_scan, total_c) - cost;
+      const int chunk = (int)max<int64_t>(kMinChunk, ((int64_t)total_c + p.plan_G - 1) / p.plan_G);
+      const int A = Q + kSegmentCost;
+      const int j1 = A / chunk, j2 = (int)(((int64_t)A + t - 1) / chunk);
+      const int ns = t > 0 ? j2 - j1 + 1 : 0;
+      const int S = block_inclusive_sum<NTHR>(ns, sm_plan_scan, total_s) - ns;
+      const int j = blockIdx.x;
+      const bool mine = t > 0 && j1 <= j && j <= j2;
+      int lo = 0, hi = 0;
+      if (mine) {
+        const int64_t start = (int64_t)j * chunk;
+        lo = (int)max(start, (int64_t)A);
+        hi = (int)min(start + chunk, (int64_t)A + t);
+        atomicMin(&sm_plan_first, S + j - j1);
+        atomicAdd(&sm_plan_n, 1);
+      }
+      if (blockIdx.z == 0 && b < p.B && (t > 0 ? j1 == j : j == 0)) {
+        int32_t* seqs = p.plan + ragged_plan_words(p.plan_G, p.B) - 2 * p.B;
+        *reinterpret_cast<int2*>(seqs + 2 * b) = make_int2(S, ns);
+      }
+      __syncthreads();
+      first = __builtin_amdgcn_readfirstlane(sm_plan_first);
+      nseg = __builtin_amdgcn_readfirstlane(sm_plan_n);
+      if (mine) sm_plan_segs[S + j - j1 - first] = make_int4(b, lo - A, hi - lo, nb);
+      __syncthreads();
+      segs = sm_plan_segs;
+      seg0 = 0;
+    } else {
+      const int2 wg = *reinterpret_cast<const int2*>(p.plan + 4 + 2 * blockIdx.x);
+      first = __builtin_amdgcn_readfirstlane(wg.x);
+      nseg = __builtin_amdgcn_readfirstlane(wg.y);
+      segs = reinterpret_cast<const int4*>(p.plan + 4 + 2 * p.plan_G);
+      seg0 = first;
+    }
     for (int k = 0; k < nseg; ++k) {
-      const int4 sg = *reinterpret_cast<const int4*>(segs + 4 * (first + k));
+      const int4 sg = segs[seg0 + k];
       const int seg_lo = __builtin_amdgcn_readfirstlane(sg.y), seg_len = __builtin_amdgcn_readfirstlane(sg.z);
       const int n = __builtin_amdgcn_readfirstlane(sg.w);
       // a segment holding all of the sequence's tiles writes the output directly
@@ -1062,75 +1191,6 @@ __global__ __launch_bounds__(256 * kMergeMaxSlices) void decode_merge_kernel(con
   *reinterpret_cast<f32x4*>(out + ((int64_t)b * Hq + h) * D + d0) = acc * inv;
 }
 
-// ---------------------------------------------------------------------------
-// Balanced plan of a ragged batch (one work-group of NTH threads: 256 for up
-// to 1024 sequences, measured ~1 us faster than 1024 there, else 1024).
-// Work is counted in tile units: a sequence with t_b > 0 visible tiles costs
-// kSegmentCost + t_b, the first kSegmentCost units standing for the fixed
-// work of starting a segment (the length and q loads before its first tile,
-// the combine and state stores after its last). Laid end to end in sequence
-// order these costs form one line of C units; with G the work-groups that
-// fill the chip once, chunk c = max(8, ceil(C / G)) and work-group j takes
-// the tiles whose unit lies in [j c, (j + 1) c), so no work-group's tiles
-// plus the segment starts inside its range cost more than c, whatever the
-// lengths. (Equal tile counts alone left the work-groups that start several
-// short sequences well behind the rest.) Sequence b's tiles occupy units
-// A_b .. A_b + t_b - 1, A_b = Q_b + kSegmentCost with Q_b the cost of the
-// sequences before it; the part of it in work-group j's range is a segment;
-// a work-group's segments are consecutive in (sequence, work-group) order,
-// which is also the order of the partial-state slots: sequence b spans
-// work-groups A_b / c .. (A_b + t_b - 1) / c and owns that many consecutive
-// slots. Written (int32 words): header {c, T, segments, ceil(C / c)}; per
-// work-group (G) {first segment, segments} (segments = 0: no work, the first
-// word is then -1); per segment (at most G + B) {b, first tile, tiles, length
-// of b}; per sequence (B) {first segment, segments}. Lengths are clamped to
-// [0, max_len] as the attention kernel clamps them; the attention kernel takes
-// a segment's length from the plan, so its first tiles go out at once.
-// ---------------------------------------------------------------------------
-constexpr int kMinChunk = kWavesPerWG;  // at least one tile per wave
-// On the hybrid block's global layer (128 sequences of 1024..32768 keys, 256
-// work-groups) the call took 142, 134, 127, 125, 129 and 132 us with a
-// segment cost of 0, 16, 32, 48, 64 and 96 tiles; once a segment's length
-// came from the plan and its first tiles went out at once, 40 measured
-// ~2.7 us faster than 48 (and 32 ~1 us, 24 no faster).
-constexpr int kSegmentCost = kRaggedSegmentCost;
-
-// The tiles the attention kernel computes for a sequence (balanced plans are
-// contiguous-buffer plans, so full windows are tiled from their first key).
-__device__ __forceinline__ int visible_tiles(int n, int window, int max_len) {
-  n = n < 0 ? 0 : (n > max_len ? max_len : n);
-  const TileRange tr = tile_range(n, window, true);
-  return tr.end - tr.begin;
-}
-__device__ __forceinline__ int sequence_cost(int t) { return t > 0 ? t + kSegmentCost : 0; }
-
-// Inclusive prefix sum over the block; `total` receives the block's sum.
-template <int NTH>
-__device__ __forceinline__ int block_inclusive_sum(int v, int* sm, int& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
-  }
-  if (lane == 63) sm[w] = v;
-  __syncthreads();
-  if (w == 0) {
-    int x = lane < NTH / 64 ? sm[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < NTH / 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    if (lane < NTH / 64) sm[lane] = x;
-  }
-  __syncthreads();
-  const int add = w > 0 ? sm[w - 1] : 0;
-  total = sm[NTH / 64 - 1];
-  __syncthreads();  // sm is reused by the next call
-  return v + add;
-}
-
 template <int NTH>
 __global__ __launch_bounds__(NTH) void decode_plan_kernel(const int32_t* __restrict__ seq_lens,
                                                                    int32_t* __restrict__ plan, int B, int window,
@@ -1201,8 +1261,6 @@ __global__ __launch_bounds__(NTH) void decode_plan_kernel(const int32_t* __restr
   }
 }
 
-// Words of the balanced plan's area (layout above decode_plan_kernel).
-constexpr size_t ragged_plan_words(size_t G, size_t B) { return 4 + 2 * G + 4 * (G + B) + 2 * B; }
 
 template <int D, int NT, bool PAGED, bool Q8, bool RAGGED>
 void launch_partitions(const DecodeParams& prm, int B, int G, hipStream_t stream) {
@@ -1371,6 +1429,7 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layo
   prm.ws_ml = nullptr;
   prm.plan = nullptr;
   prm.plan_G = 0;
+  prm.plan_inline = 0;
   prm.fixed_tiles = g_fixed_tiles.load(std::memory_order_relaxed) ? 1 : 0;
   prm.B = B;
   const int G = plan.ragged_groups;
@@ -1386,13 +1445,17 @@ int launch_decode(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& layo
     prm.ws_o = reinterpret_cast<float*>(ws);
     prm.plan = plan_area;
     prm.plan_G = G;
-    if (B <= 1024)
-      hipLaunchKernelGGL(decode_plan_kernel<256>, dim3(1), dim3(256), 0, stream, seq_lens, plan_area, B, window,
-                         prm.max_len, G);
-    else
-      hipLaunchKernelGGL(decode_plan_kernel<1024>, dim3(1), dim3(1024), 0, stream, seq_lens, plan_area, B, window,
-                         prm.max_len, G);
-    if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
+    // small batches are planned inside the attention kernel
+    prm.plan_inline = B <= kInlinePlanMaxB ? 1 : 0;
+    if (!prm.plan_inline) {
+      if (B <= 1024)
+        hipLaunchKernelGGL(decode_plan_kernel<256>, dim3(1), dim3(256), 0, stream, seq_lens, plan_area, B, window,
+                           prm.max_len, G);
+      else
+        hipLaunchKernelGGL(decode_plan_kernel<1024>, dim3(1), dim3(1024), 0, stream, seq_lens, plan_area, B,
+                           window, prm.max_len, G);
+      if (hipGetLastError() != hipSuccess) return MQA_ERR_HIP;
+    }
   } else if (plan.num_parts > 1) {
     const size_t slots = (size_t)B * (size_t)plan.num_parts * (size_t)Hq;
     char* ws = static_cast<char*>(workspace);

@@ -116,9 +116,12 @@ def test_append_ragged_hybrid_global():
 
 @pytest.mark.parametrize("case", ["hybrid", "mixed_w4096", "2500", "sparse"])
 def test_plan_words_match_the_model(case):
-    """The planning kernel's words (start of the workspace, which is filled
-    with 0xff first) against the host model of the documented layout; the
-    segment slots past the last used one are not compared."""
+    """The plan words (start of the workspace, which is filled with 0xff
+    first) against the host model of the documented layout. Batches of more
+    than 512 sequences are planned by the planning kernel, which writes every
+    word (the segment slots past the last used one are not compared);
+    smaller ones inside the attention kernel, which writes only the
+    per-sequence words the merge kernel reads."""
     import mqa_attention_int8_amd as m
     from plan_model import n_words, plan_words, unpack
     window, Hq, D = 0, 32, 128
@@ -149,7 +152,10 @@ def test_plan_words_match_the_model(case):
     want, S = plan_words(lens, window, L, G)
     gh, gw, gs, gq = unpack(got, G, B)
     wh, ww, ws_, wq = unpack(want, G, B)
-    assert np.array_equal(gh, wh), (gh, wh)
-    assert np.array_equal(gw, ww)
-    assert np.array_equal(gs[:S], ws_[:S])
     assert np.array_equal(gq, wq)
+    if B > 512:
+        assert np.array_equal(gh, wh), (gh, wh)
+        assert np.array_equal(gw, ww)
+        assert np.array_equal(gs[:S], ws_[:S])
+    else:
+        assert np.all(gh == -1) and np.all(gw == -1)   # the planning kernel did not run
