@@ -796,8 +796,8 @@ def main():
         "block_step_median_us": hyb["block_step"]["median_us"],
         "roofline": {"bound": "hbm", "achieved": hyb["global_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": hyb["global_GBps"] / HBM_PEAK_GBPS, "traffic": counted_traffic(),
-                     "kernel": "global layer of the block: mqa_decode_append_ragged (decode_plan_kernel + "
-                               "decode_partition_kernel + decode_merge_kernel)",
+                     "kernel": "global layer of the block: mqa_decode_append_ragged (decode_partition_kernel, "
+                               "which plans its own range, + decode_merge_kernel)",
                      "algorithmic_bytes_per_launch": hyb["global_kv_bytes"],
                      "avg_launch_us": g["mean_us"], "median_launch_us": g["median_us"],
                      "launch_us_min_max": [g["min_us"], g["max_us"]], "replays": g["replays"]},
