@@ -159,3 +159,11 @@ def test_plan_words_match_the_model(case):
         assert np.array_equal(gs[:S], ws_[:S])
     else:
         assert np.all(gh == -1) and np.all(gw == -1)   # the planning kernel did not run
+
+
+@pytest.mark.parametrize("B", [512, 513])
+def test_plan_inside_and_outside_the_kernel(B):
+    """512 sequences are planned inside the attention kernel, 513 by the
+    planning kernel: both against the oracle, lengths 0..2000 keys."""
+    lens = synth.ragged_lens(synth.rng(104, synth.T_LENS, B), B, 0, 2000)
+    ragged_case(104, B, 2016, 8, 64, lens, 0, f"B{B} plan switch")
