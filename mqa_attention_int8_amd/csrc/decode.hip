@@ -214,9 +214,10 @@ __device__ __forceinline__ uint32_t stage_lane_offset(int lane) {
 }
 
 // Direct-to-LDS buffer loads: each lane's 16 (or 4) bytes land at
-// lds + 16 * lane (or 4 * lane); the 16-byte form is non-temporal.
-__device__ __forceinline__ void lds_load16_nt(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, kCachePolicyNT);
+// lds + 16 * lane (or 4 * lane); the 16-byte form optionally non-temporal.
+template <bool NT>
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, NT ? kCachePolicyNT : 0);
 }
 __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, soff, 0, 0);
@@ -225,18 +226,17 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, char* lds, u
 // Issue the loads of the tile whose first row is `base` (scalar offset) into
 // `slot`. The tile base enters as the scalar offset, which the range check of
 // a buffer load does not cover: only tiles wholly inside the buffer exist.
-template <int D>
+template <int D, bool NT>
 __device__ __forceinline__ void stage_tile(char* slot, const SeqBuffers& sb, uint32_t lane_kv, uint32_t lane_sc,
                                            int base, bool exists) {
   const uint32_t vk = exists ? lane_kv : kNowhere;
   const uint32_t vs = exists ? lane_sc : kNowhere;
   const uint32_t kv_s = __builtin_amdgcn_readfirstlane(exists ? (uint32_t)base * D : 0u);
   const uint32_t sc_s = __builtin_amdgcn_readfirstlane(exists ? (uint32_t)base * 4 : 0u);
-  // K and V are read once per call: non-temporal loads (measured faster)
 #pragma unroll
-  for (int j = 0; j < Slot<D>::kKV / 1024; ++j) lds_load16_nt(sb.k, slot + j * 1024, vk + j * 1024, kv_s);
+  for (int j = 0; j < Slot<D>::kKV / 1024; ++j) lds_load16<NT>(sb.k, slot + j * 1024, vk + j * 1024, kv_s);
 #pragma unroll
-  for (int j = 0; j < Slot<D>::kKV / 1024; ++j) lds_load16_nt(sb.v, slot + Slot<D>::kOffV + j * 1024, vk + j * 1024, kv_s);
+  for (int j = 0; j < Slot<D>::kKV / 1024; ++j) lds_load16<NT>(sb.v, slot + Slot<D>::kOffV + j * 1024, vk + j * 1024, kv_s);
   lds_load4(sb.ks, slot + Slot<D>::kOffKs, vs, sc_s);
   lds_load4(sb.vs, slot + Slot<D>::kOffVs, vs, sc_s);
 }
@@ -772,6 +772,11 @@ void decode_partition_kernel(DecodeParams p) {
   const int h0 = p.heads_per_group * (int)blockIdx.z;   // first head of this group
   const int Hg = min(Hq - h0, min(p.heads_per_group, NT * 16));    // heads of this group
 
+  // A global layer's K and V are read once per call: non-temporal loads
+  // (measured faster). A window's keys are read again by the next layer that
+  // shares the buffer, in the same step, and by the next step: default
+  // policy, so they may stay in the caches.
+  constexpr bool kStreamKV = !WINDOWED;
   const uint32_t lane_kv = stage_lane_offset<D>(lane);
   const uint32_t lane_sc = (uint32_t)(lane & 31) * 4;
 
@@ -854,7 +859,7 @@ void decode_partition_kernel(DecodeParams p) {
   char* const s1 = sm_s1[wave];
   if (!WINDOWED && !PAGED && !RAGGED) {
     const int t0 = seg_lo + wave;
-    stage_tile<D>(s0, sb, lane_kv, lane_sc, t0 * kTileKeys, wave < seg_len && (t0 + 1) * kTileKeys <= p.L_cap);
+    stage_tile<D, kStreamKV>(s0, sb, lane_kv, lane_sc, t0 * kTileKeys, wave < seg_len && (t0 + 1) * kTileKeys <= p.L_cap);
   }
 
   int n = __builtin_amdgcn_readfirstlane(n_raw);  // same for the whole work-group
@@ -894,7 +899,7 @@ void decode_partition_kernel(DecodeParams p) {
   // Staging loads of tile i of the partition (i >= count: nothing is read).
   const auto stage = [&](char* slot, int i) {
     if (!PAGED) {
-      stage_tile<D>(slot, sb, lane_kv, lane_sc, org + (pt0 + i) * kTileKeys, i < count);
+      stage_tile<D, kStreamKV>(slot, sb, lane_kv, lane_sc, org + (pt0 + i) * kTileKeys, i < count);
     } else {
       SeqBuffers tsb;
       const int64_t row = i < count ? phys_row((pt0 + i) * kTileKeys) : 0;
@@ -903,7 +908,7 @@ void decode_partition_kernel(DecodeParams p) {
       tsb.v = make_rsrc(p.v + row * D, kvb);
       tsb.ks = make_rsrc(p.ks + row, scb);
       tsb.vs = make_rsrc(p.vs + row, scb);
-      stage_tile<D>(slot, tsb, lane_kv, lane_sc, 0, i < count);
+      stage_tile<D, kStreamKV>(slot, tsb, lane_kv, lane_sc, 0, i < count);
     }
   };
   if (WINDOWED || PAGED || RAGGED) stage(s0, wave);
