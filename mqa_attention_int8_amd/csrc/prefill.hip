@@ -24,7 +24,8 @@
 //    them; both with 16-byte chunks XOR-swizzled so the MFMA operand reads
 //    from LDS are free of bank conflicts; plus s_k * scale * log2(e) per key.
 //    E is a per-sequence power of two with 2^E >= max s_v (a small first
-//    pass), which keeps V'' in fp16's range; it is undone on the output.
+//    pass, or for a window the stage work-groups themselves), which keeps
+//    V'' in fp16's range; it is undone on the output.
 //  * Attention pass: work-group = 8 waves x 32 rows, one per compute unit;
 //    staged tiles stream global -> LDS with direct-to-LDS loads (no
 //    registers) through four buffers, two tiles ahead of the one being
@@ -93,6 +94,7 @@ struct PrefillParams {
   int32_t ntiles;       // tiles per sequence in the workspace
   int32_t P_max;        // prefix lengths are clamped to [0, P_max] (workspace and cache bounds)
   int32_t row_tiles;    // attention work-groups per sequence
+  int32_t inline_e;     // != 0: each stage work-group derives E itself (short visible ranges)
   float scale_log2;
 };
 
@@ -118,6 +120,8 @@ __device__ __forceinline__ int first_needed_key(int P, int window) {
 // ---------------------------------------------------------------------------
 constexpr int kExpThreads = 1024;
 constexpr int kExpUnroll = 4;
+// Visible ranges up to this many keys get E from the stage pass itself.
+constexpr int kInlineExpKeys = 4096;
 __global__ __launch_bounds__(kExpThreads) void prefill_exponent_kernel(PrefillParams p) {
   const int b = blockIdx.x, tid = threadIdx.x;
   __shared__ float red[kExpThreads / kWave];
@@ -173,6 +177,28 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
   const int base = t * kKeys;
   char* tile = p.stage + ((int64_t)b * p.ntiles + t) * StagedTile<D>::kBytes;
 
+  // E for the value scaling: from the exponent pass, or (a visible range of
+  // at most kInlineExpKeys keys) the same maximum formed here by every
+  // work-group of the sequence, the one of its first tile writing it for the
+  // attention pass.
+  float e_seq;
+  if (p.inline_e) {
+    __shared__ float red[256 / kWave];
+    float m = 0.f;
+    for (int j = kbeg + tid; j < kend; j += 256) m = fmaxf(m, fabsf(p.vs[key_row_of<PAGED>(p, b, j)]));
+#pragma unroll
+    for (int s_ = 32; s_ >= 1; s_ >>= 1) m = fmaxf(m, __shfl_xor(m, s_, kWave));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int e = 0;
+    if (m > 0.f && m < INFINITY) (void)frexpf(m, &e);
+    e_seq = (float)e;
+    if (t == t_lo && tid == 0) p.seq_e[b] = e_seq;
+  } else {
+    e_seq = p.seq_e[b];
+  }
+
   // K: thread = (key, quarter of the row); 16-byte chunk c of row `key` is
   // stored at chunk c ^ (key & kSwzK).
   {
@@ -204,7 +230,7 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
   // overflow fp16, and its zero weight times infinity would be NaN.
   {
     constexpr int DQ = D / 4;   // 4-column groups
-    const float rE = exp2f(-p.seq_e[b]);
+    const float rE = exp2f(-e_seq);
     for (int it = tid; it < 8 * DQ; it += 256) {
       const int grp = it / DQ, dq = it % DQ;
       const int ks = grp >> 2, g = grp & 3;
@@ -628,7 +654,10 @@ int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& lay
   const int64_t grid = (int64_t)prm.row_tiles * B;
   if (grid > 0x7fffffff) return MQA_ERR_SHAPE;
   const dim3 sgrid(prm.ntiles, B);
-  hipLaunchKernelGGL(prefill_exponent_kernel, dim3(B), dim3(kExpThreads), 0, stream, prm);
+  // A short visible range (a window) is scanned by the stage work-groups
+  // themselves: one kernel launch less.
+  prm.inline_e = (window > 0 && (int64_t)window + C <= kInlineExpKeys) ? 1 : 0;
+  if (!prm.inline_e) hipLaunchKernelGGL(prefill_exponent_kernel, dim3(B), dim3(kExpThreads), 0, stream, prm);
   if (D == 128) {
     if (prm.table)
       hipLaunchKernelGGL((prefill_stage_kernel<128, true>), sgrid, dim3(256), 0, stream, prm);
