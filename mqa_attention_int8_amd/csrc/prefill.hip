@@ -45,6 +45,8 @@
 //    tiles are masked per element; work-groups of one sequence share an XCD.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -160,19 +162,23 @@ __device__ __forceinline__ int64_t key_row_of(const PrefillParams& p, int b, int
 }
 
 // ---------------------------------------------------------------------------
-// Stage pass: grid (ntiles, B), 256 threads, one 64-key tile per work-group.
+// Stage pass: grid (tiles, B), 256 threads, one 64-key tile per work-group
+// (a window: only the tiles its needed keys can span, from the first).
 // Keys past the last one (kend) are read at row kend - 1 and zeroed after the
 // load, so every load of a thread is issued before the first wait (loads
 // under per-key conditions each waited for the previous one).
 // ---------------------------------------------------------------------------
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillParams p) {
-  const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int b = blockIdx.y, tid = threadIdx.x;
   const int P = clampP(__builtin_amdgcn_readfirstlane(p.prefix_lens[b]), p.P_max);
   const int kend = P + p.C;                            // keys [0, kend) exist
   const int kbeg = first_needed_key(P, p.window);      // no query of the chunk sees a key before it
   const int t_lo = kbeg / kKeys;
   const int t_hi = (kend + kKeys - 1) / kKeys;
+  // A window's grid covers only the tiles one window and the chunk can span,
+  // counted from the sequence's first needed tile.
+  const int t = p.window > 0 ? t_lo + (int)blockIdx.x : (int)blockIdx.x;
   if (t < t_lo || t >= t_hi) return;
   const int base = t * kKeys;
   char* tile = p.stage + ((int64_t)b * p.ntiles + t) * StagedTile<D>::kBytes;
@@ -653,7 +659,9 @@ int launch_prefill(const uint16_t* q, const mqa_kv_view& kv, const KVLayout& lay
   prm.row_tiles = (int)((rows + kRowsPerWG - 1) / kRowsPerWG);
   const int64_t grid = (int64_t)prm.row_tiles * B;
   if (grid > 0x7fffffff) return MQA_ERR_SHAPE;
-  const dim3 sgrid(prm.ntiles, B);
+  // a window's needed keys [P - W + 1, P + C) span at most this many tiles
+  const int64_t win_tiles = window > 0 ? ((int64_t)window - 1 + C + kKeys - 1) / kKeys + 1 : prm.ntiles;
+  const dim3 sgrid((unsigned)std::min<int64_t>(prm.ntiles, win_tiles), B);
   // A short visible range (a window) is scanned by the stage work-groups
   // themselves: one kernel launch less.
   prm.inline_e = (window > 0 && (int64_t)window + C <= kInlineExpKeys) ? 1 : 0;
