@@ -993,13 +993,19 @@ void decode_partition_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  for (int job = threadIdx.x; job < NT * 256; job += NTHR) {
+  // NT * 256 jobs over the work-group's threads: with 16 heads two threads
+  // share a job, each combining half of its dims.
+  constexpr int SPLIT = NTHR / (NT * 256);
+  constexpr int DPS = DPL / SPLIT;
+  static_assert(SPLIT * NT * 256 == NTHR && DPS * SPLIT == DPL && DPS % 2 == 0, "combine split");
+  {
+    const int job = threadIdx.x / SPLIT, part = threadIdx.x % SPLIT;
     const int nt = job >> 8;
     const int gq = (job >> 6) & 3;
     const int cc = (job >> 2) & 15;
     const int rr = job & 3;
     const int h = 16 * nt + cc;
-    const int d0 = DPL * (4 * gq + rr);
+    const int d0 = DPL * (4 * gq + rr) + DPS * part;
     float mw[WV], f[WV];
     float M = -INFINITY;
 #pragma unroll
@@ -1014,14 +1020,15 @@ void decode_partition_kernel(DecodeParams p) {
       L += f[w];
     }
     const float invL = L > 0.f ? 1.f / L : 0.f;
-    float o[DPL];
+    float o[DPS];
 #pragma unroll
-    for (int mt = 0; mt < DPL; ++mt) {
+    for (int mi = 0; mi < DPS; ++mi) {
+      const int mt = DPS * part + mi;
       float acc = 0.f;
 #pragma unroll
       for (int w = 0; w < WV; ++w)
         acc += f[w] * parked(w, nt * DPL + mt)[(16 * gq + cc) * 4 + rr];
-      o[mt] = acc * invL;  // normalised: the output itself, or this partition's share
+      o[mi] = acc * invL;  // normalised: the output itself, or this partition's share
     }
     if (h < Hg) {
       float* dst;
@@ -1029,11 +1036,16 @@ void decode_partition_kernel(DecodeParams p) {
         dst = p.out + ((int64_t)b * Hq + h0 + h) * D + d0;
       } else {
         dst = p.ws_o + (slot * Hq + h0 + h) * D + d0;
-        if (gq == 0 && rr == 0) p.ws_ml[slot * Hq + h0 + h] = make_float2(M, L);
+        if (part == 0 && gq == 0 && rr == 0) p.ws_ml[slot * Hq + h0 + h] = make_float2(M, L);
       }
+      if constexpr (DPS % 4 == 0) {
 #pragma unroll
-      for (int u = 0; u < DPL; u += 4)
-        *reinterpret_cast<f32x4*>(dst + u) = f32x4{o[u], o[u + 1], o[u + 2], o[u + 3]};
+        for (int u = 0; u < DPS; u += 4)
+          *reinterpret_cast<f32x4*>(dst + u) = f32x4{o[u], o[u + 1], o[u + 2], o[u + 3]};
+      } else {
+#pragma unroll
+        for (int u = 0; u < DPS; u += 2) *reinterpret_cast<float2*>(dst + u) = make_float2(o[u], o[u + 1]);
+      }
     }
   }
   };
